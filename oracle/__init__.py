@@ -1,0 +1,13 @@
+"""fp64 CPU oracle for decode-phase paged attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``, never by the library.
+"""
+
+from .decode import (  # noqa: F401
+    attend,
+    decode_attention,
+    dequantize_rows,
+    gather_sequence,
+    kv_head_of,
+)
