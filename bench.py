@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Decode-phase paged attention on one MI355X: KV-read GB/s and us/step.
+
+One step is one decode_attn call over the whole batch (the split kernel, plus
+the merge kernel when the plan has more than one partition): one layer's decode
+attention. The default workload is the Llama-2-7B-shaped MHA batch (batch 48,
+32 query = 32 KV heads, head_dim 128, seq_lens uniform in [18, 563], 16-token
+pages in a shuffled pool, fp16 K/V ~ N(0, 1)); --config picks another preset.
+
+Inputs are resident in HBM before timing starts. To keep the 256 MB Infinity
+Cache from serving the KV reads, the step rotates over R replicas of the page
+pools totalling at least 1 GiB. Throughput counts algorithmic KV bytes only:
+sum_b L_b * Hkv * 2 * D * elem (plus the fp32 row scales for INT8).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
+METRIC = "decode-attn KV-read GB/s (fraction of MI355X HBM peak) + µs/step"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_phase_attention_paged_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    path = os.path.join(PROFILES, f"decode_split_{workload_name}_pmc.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return float(fields["traffic_bytes_per_launch"]), path
+    except (KeyError, ValueError):
+        return None, "summary lacks traffic_bytes_per_launch"
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The fp64 oracle as it stands, timed on the host over a bounded sample."""
+    import numpy as np
+    import oracle
+    from decode_phase_attention_paged_amd.workload import kv_read_bytes
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    c = w.config
+    # Sample: a prefix of the batch sized to fit the budget (at least one sequence).
+    t0 = time.perf_counter()
+    oracle.decode_attention(w.q[:1], w.k_pages, w.v_pages, w.block_table[:1], w.seq_lens[:1],
+                            w.scale, w.k_scale, w.v_scale)
+    per_token = max((time.perf_counter() - t0) / max(int(w.seq_lens[0]), 1), 1e-9)
+    total_tokens = int(w.seq_lens.sum())
+    n = c.batch
+    if per_token * total_tokens > budget_s:
+        cum = np.cumsum(w.seq_lens.astype(np.int64))
+        n = max(1, int(np.searchsorted(cum, budget_s / per_token)))
+    elem = 1 if c.kv_dtype == "int8" else 2
+    sample_bytes = kv_read_bytes(w.seq_lens[:n], c.n_kv_heads, c.head_dim, elem,
+                                 4 if c.kv_dtype == "int8" else 0)
+    reps, spent = 0, 0.0
+    while reps < 1 or (spent < budget_s and reps < 50):
+        t0 = time.perf_counter()
+        oracle.decode_attention(w.q[:n], w.k_pages, w.v_pages, w.block_table[:n], w.seq_lens[:n],
+                                w.scale, w.k_scale, w.v_scale)
+        spent += time.perf_counter() - t0
+        reps += 1
+    gbs = sample_bytes * reps / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {c.batch} sequences x {reps} repetitions "
+                      f"({sample_bytes * reps / 1e9:.3f} GB of KV in {spent:.1f} s)",
+            "seconds_per_full_step": round(spent / reps * total_tokens /
+                                           max(int(w.seq_lens[:n].sum()), 1), 4)}
+
+
+def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
+    """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library runs decode attention on a single "
+              "MI355X, and multi-GPU sharding is a design note only; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from decode_phase_attention_paged_amd import binding
+    from decode_phase_attention_paged_amd.workload import CONFIGS, generate
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    lib = binding.load_library()
+    cfg = CONFIGS[args.config]
+    log(f"generating {cfg.name} ...")
+    w = generate(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, bt, sl = t(w.q), t(w.block_table), t(w.seq_lens)
+    pool_bytes = 2 * w.k_pages.nbytes + (2 * w.k_scale.nbytes if w.k_scale is not None else 0)
+    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    pools = []
+    for _ in range(reps):
+        pools.append((t(w.k_pages), t(w.v_pages), t(w.k_scale), t(w.v_scale)))
+    out = torch.empty(w.q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    kv_type = binding.KV_INT8 if cfg.kv_dtype == "int8" else binding.KV_FP16
+    num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    splits, pps = binding.plan_splits(cfg.batch, cfg.max_blocks_per_seq, cfg.n_kv_heads,
+                                      cfg.block_size, args.splits, num_cus)
+
+    # Marshal the arguments once; the timed loop calls the C ABI directly.
+    p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    call_args = []
+    workspace = None
+    if args.splits:
+        need = binding.workspace_size(cfg.batch, cfg.n_q_heads, cfg.head_dim, splits)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    for kp, vp, ks, vs in pools:
+        common = (p(q), p(kp), p(vp), p(ks), p(vs), p(bt), p(sl), cfg.batch,
+                  cfg.max_blocks_per_seq, w.num_pages, cfg.n_q_heads, cfg.n_kv_heads,
+                  cfg.head_dim, cfg.block_size, kv_type, float(w.scale), p(out))
+        if args.splits:
+            call_args.append(("ex", common + (None, args.splits, p(workspace),
+                                              workspace.numel(), s_handle)))
+        else:
+            call_args.append(("auto", common + (s_handle,)))
+
+    def step(i):
+        kind, a = call_args[i % reps]
+        st = lib.decode_attn(*a) if kind == "auto" else lib.decode_attn_ex(*a)
+        if st != 0:
+            raise RuntimeError(f"decode_attn failed: {binding.STATUS.get(st, st)}")
+
+    log(f"plan: splits={splits} pages_per_split={pps} replicas={reps} "
+        f"pool={pool_bytes / 1e6:.1f} MB kv_bytes/step={w.kv_bytes / 1e6:.1f} MB")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    begin = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start_ev.record(stream)
+    for i in range(args.steps):
+        begin[i].record(stream)
+        step(args.warmup + i)
+        end[i].record(stream)
+    stop_ev.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start_ev.elapsed_time(stop_ev)
+    launch_ms = [b.elapsed_time(e) for b, e in zip(begin, end)]
+    avg_launch_s = float(np.mean(launch_ms)) / 1e3
+    ms_per_step = total_ms / args.steps
+    gbs = w.kv_bytes * args.steps / (total_ms / 1e3) / 1e9
+    achieved = w.kv_bytes / avg_launch_s / 1e9
+    log(f"steps={args.steps} total={total_ms:.3f} ms (wall {wall * 1e3:.1f} ms) "
+        f"us/step={ms_per_step * 1e3:.2f} per-launch avg={avg_launch_s * 1e6:.2f} us "
+        f"p50={np.median(launch_ms) * 1e3:.2f} us GB/s={gbs:.1f} ({gbs / HBM_PEAK_GBS:.3f} of peak)")
+
+    traffic, traffic_src = read_traffic(cfg.name)
+    log(f"traffic: {traffic} ({traffic_src})")
+    baseline = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        baseline = cpu_baseline(w)
+        log(f"cpu baseline: {baseline}")
+
+    record = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if cfg.kv_dtype == "fp16" else "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "batch": cfg.batch, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+            "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
+            "seq_lens": f"uniform [{cfg.len_lo}, {cfg.len_hi}], seed {w.seed}",
+            "tokens": int(w.seq_lens.sum()), "num_pages": w.num_pages,
+            "num_splits": splits, "pages_per_split": pps, "replicas": reps,
+            "kv_bytes_per_step": int(w.kv_bytes),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "split_kernel" + (" + merge_kernel" if splits > 1 else ""),
+            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+        },
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

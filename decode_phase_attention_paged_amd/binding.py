@@ -1,0 +1,204 @@
+"""ctypes binding over the C ABI in include/decode_attn.h.
+
+Argument marshalling only: torch tensors supply device pointers and the current
+HIP stream; every step of the computation runs in the HIP library. There is no
+fallback of any kind: if the library is missing or a call fails, this module
+raises.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch has already mapped (both carry the soname
+libamdhip64.so.7), and torch's stream handles are valid inside it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
+
+KV_FP16 = 0
+KV_INT8 = 1
+STATUS = {0: "DECODE_ATTN_OK", 1: "DECODE_ATTN_ERR_INVALID_ARGUMENT",
+          2: "DECODE_ATTN_ERR_UNSUPPORTED", 3: "DECODE_ATTN_ERR_WORKSPACE",
+          4: "DECODE_ATTN_ERR_HIP"}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
+    "decode_attn_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
+                            _P, _I, _P, _SZ, _P]),
+    "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "decode_attn_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "decode_attn_status_string": (ctypes.c_char_p, [_I]),
+    "decode_attn_version": (_I, []),
+}
+
+_lib = None
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load (once) and return the ctypes handle of libdecode_attn.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m decode_phase_attention_paged_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DecodeAttnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _validate(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out):
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_attn runs on the GPU only; q is on " + str(dev))
+    named = dict(q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+                 seq_lens=seq_lens, out=out)
+    if k_scale is not None or v_scale is not None:
+        named.update(k_scale=k_scale, v_scale=v_scale)
+    for name, t in named.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype != torch.float16 or q.dim() != 3:
+        raise ValueError("q must be fp16 [batch, n_q_heads, head_dim]")
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages must both be [num_pages, n_kv_heads, block_size, head_dim]")
+    if k_pages.dtype == torch.float16:
+        kv = KV_FP16
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("row scales are only for int8 caches")
+    elif k_pages.dtype == torch.int8:
+        kv = KV_INT8
+        if k_scale is None or v_scale is None:
+            raise ValueError("int8 caches need k_scale and v_scale")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_pages.shape[:3]):
+                raise ValueError("row scales must be fp32 [num_pages, n_kv_heads, block_size]")
+    else:
+        raise ValueError("k_pages must be fp16 or int8")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [batch, max_blocks_per_seq]")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (q.shape[0],):
+        raise ValueError("seq_lens must be int32 [batch]")
+    if block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table rows must equal batch")
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be fp32 [batch, n_q_heads, head_dim]")
+    if k_pages.shape[3] != q.shape[2]:
+        raise ValueError("head_dim of q and the pages differ")
+    return kv
+
+
+def _common(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out):
+    kv = _validate(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out)
+    batch, n_q, head_dim = q.shape
+    num_pages, n_kv, block_size, _ = k_pages.shape
+    return (kv, batch, block_table.shape[1], num_pages, n_q, n_kv, head_dim, block_size)
+
+
+def decode_attn(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=None,
+                v_scale=None, out=None):
+    """Decode attention with the library's own split plan and workspace.
+
+    Returns ``out`` (fp32 [batch, n_q_heads, head_dim]); the work is enqueued on
+    torch's current stream of q's device.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    kv, batch, mb, np_, n_q, n_kv, d, bs = _common(q, k_pages, v_pages, block_table, seq_lens,
+                                                   k_scale, v_scale, out)
+    with torch.cuda.device(q.device):
+        st = lib.decode_attn(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                             _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), batch, mb, np_,
+                             n_q, n_kv, d, bs, kv, float(scale), _ptr(out), _stream(q.device))
+    _check(st, "decode_attn")
+    return out
+
+
+def plan_splits(batch: int, max_blocks_per_seq: int, n_kv_heads: int, block_size: int = 16,
+                requested_splits: int = 0, num_cus: int = 0):
+    """Return (num_splits, pages_per_split) as the library would use them."""
+    lib = load_library()
+    s, p = _I(0), _I(0)
+    _check(lib.decode_attn_plan(batch, max_blocks_per_seq, n_kv_heads, block_size,
+                                requested_splits, num_cus, ctypes.byref(s), ctypes.byref(p)),
+           "decode_attn_plan")
+    return s.value, p.value
+
+
+def workspace_size(batch: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(load_library().decode_attn_workspace_size(batch, n_q_heads, head_dim, num_splits))
+
+
+def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=None,
+                   v_scale=None, out=None, lse_out=None, num_splits=0, workspace=None):
+    """Decode attention with an explicit split request and caller-owned workspace.
+
+    ``num_splits`` 0 lets the library choose. ``workspace`` (a uint8 device
+    tensor) is allocated here, through torch, when not given. ``lse_out``
+    (fp32 [batch, n_q_heads]) receives the natural-log log-sum-exp of the
+    scores when given. Returns ``out``.
+    """
+    lib = load_library()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    kv, batch, mb, np_, n_q, n_kv, d, bs = _common(q, k_pages, v_pages, block_table, seq_lens,
+                                                   k_scale, v_scale, out)
+    if lse_out is not None:
+        if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (batch, n_q)
+                or not lse_out.is_contiguous() or lse_out.device != q.device):
+            raise ValueError("lse_out must be contiguous fp32 [batch, n_q_heads] on q's device")
+    cus = 0
+    if num_splits == 0:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    splits, _ = plan_splits(batch, mb, n_kv, bs, num_splits, cus)
+    need = workspace_size(batch, n_q, d, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        st = lib.decode_attn_ex(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), batch, mb, np_,
+                                n_q, n_kv, d, bs, kv, float(scale), _ptr(out), _ptr(lse_out),
+                                num_splits, _ptr(workspace), ws_bytes, _stream(q.device))
+    _check(st, "decode_attn_ex")
+    return out

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Bar (the decode-attention tolerance for fp32 outputs): elementwise
+|gpu - oracle| <= 2e-3 + 1e-2 * |oracle|. Every call goes through the C ABI.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_phase_attention_paged_amd.workload import CONFIGS, Config, generate
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need an MI355X"
+    return t
+
+
+@pytest.fixture(scope="module")
+def lib(torch):
+    from decode_phase_attention_paged_amd import binding
+    return binding
+
+
+def to_dev(torch, w):
+    dev = torch.device("cuda:0")
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return dict(q=t(w.q), k_pages=t(w.k_pages), v_pages=t(w.v_pages), k_scale=t(w.k_scale),
+                v_scale=t(w.v_scale), block_table=t(w.block_table), seq_lens=t(w.seq_lens))
+
+
+def gpu_run(torch, lib, w, num_splits=0, lse=True, dev_inputs=None):
+    d = dev_inputs or to_dev(torch, w)
+    lse_out = torch.empty(w.q.shape[:2], dtype=torch.float32, device="cuda:0") if lse else None
+    out = lib.decode_attn_ex(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
+                             w.scale, k_scale=d["k_scale"], v_scale=d["v_scale"],
+                             lse_out=lse_out, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse_out.cpu().numpy() if lse else None)
+
+
+def assert_parity(got, ref, what=""):
+    diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    bound = ATOL + RTOL * np.abs(ref.astype(np.float64))
+    bad = ~(diff <= bound)
+    print(f"{what}: max|d|={np.nanmax(diff) if diff.size else 0:.3e}", flush=True)
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance, "
+                           f"max|d|={np.nanmax(diff):.3e}")
+
+
+def assert_lse(got, ref, what=""):
+    empty = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), empty), what
+    np.testing.assert_allclose(got[~empty], ref[~empty], rtol=1e-4, atol=1e-3, err_msg=what)
+
+
+def oracle_run(w):
+    return oracle.decode_attention(w.q, w.k_pages, w.v_pages, w.block_table, w.seq_lens, w.scale,
+                                   w.k_scale, w.v_scale)
+
+
+SMALL = Config(0, "small_gqa", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128, block_size=16,
+               len_lo=1, len_hi=300, kv_dtype="fp16")
+
+
+# ------------------------------------------------------------------ small, every kernel variant
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_small_all_variants(torch, lib, kv, group, splits):
+    cfg = SMALL.with_(kv_dtype=kv, n_q_heads=2 * group, n_kv_heads=2)
+    w = generate(cfg, seed=100 + group)
+    print(f"case kv={kv} G={group} S={splits} lens={w.seq_lens.tolist()}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w, num_splits=splits)
+    assert_parity(got, ref, f"{kv} G={group} S={splits}")
+    assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 19])
+def test_split_counts_and_determinism(torch, lib, splits):
+    w = generate(SMALL, seed=7)
+    ref, ref_lse = oracle_run(w)
+    d = to_dev(torch, w)
+    a, la = gpu_run(torch, lib, w, num_splits=splits, dev_inputs=d)
+    b, lb = gpu_run(torch, lib, w, num_splits=splits, dev_inputs=d)
+    assert_parity(a, ref, f"S={splits}")
+    assert_lse(la, ref_lse, "lse")
+    assert np.array_equal(a, b) and np.array_equal(la, lb), "same inputs, same S: not bitwise equal"
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_edge_lengths_and_nan_canaries(torch, lib, kv):
+    # Empty, single-token, page-boundary and full caches in one batch; every slot no token
+    # owns (and 5 pages nobody references) holds NaN.
+    lens = np.array([0, 1, 15, 16, 17, 31, 32, 33, 299, 300, 0, 2], dtype=np.int32)
+    cfg = SMALL.with_(kv_dtype=kv, batch=len(lens), len_lo=0)
+    w = generate(cfg, seed=11, seq_lens=lens, extra_pages=5, poison=True)
+    print(f"case edge kv={kv}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    assert np.isfinite(ref).all()
+    for splits in (1, 4, 19):
+        got, lse = gpu_run(torch, lib, w, num_splits=splits)
+        assert np.isfinite(got).all(), f"S={splits}: a NaN canary leaked into the output"
+        assert_parity(got, ref, f"edge {kv} S={splits}")
+        assert_lse(lse, ref_lse, "lse")
+        assert np.all(got[lens == 0] == 0)
+
+
+def test_page_permutation_is_bitwise_invariant(torch, lib):
+    w = generate(SMALL, seed=12, extra_pages=3)
+    a, _ = gpu_run(torch, lib, w, num_splits=2)
+    perm = np.random.default_rng(0).permutation(w.num_pages)
+    k2 = np.empty_like(w.k_pages)
+    v2 = np.empty_like(w.v_pages)
+    k2[perm] = w.k_pages
+    v2[perm] = w.v_pages
+    w.k_pages, w.v_pages = k2, v2
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    b, _ = gpu_run(torch, lib, w, num_splits=2)
+    assert np.array_equal(a, b)
+
+
+def test_gqa_matches_repeated_mha(torch, lib):
+    w = generate(SMALL, seed=13)
+    a, _ = gpu_run(torch, lib, w, num_splits=1)
+    group = SMALL.n_q_heads // SMALL.n_kv_heads
+    w.k_pages = np.repeat(w.k_pages, group, axis=1)
+    w.v_pages = np.repeat(w.v_pages, group, axis=1)
+    b, _ = gpu_run(torch, lib, w, num_splits=1)
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
+
+
+def test_int8_unit_scales_match_fp16_on_same_integers(torch, lib):
+    cfg = SMALL.with_(kv_dtype="int8")
+    w = generate(cfg, seed=14)
+    w.scale = 0.001  # raw int8 dot products are ~1e3; keep the softmax soft
+    w.k_scale = np.ones_like(w.k_scale)
+    w.v_scale = np.ones_like(w.v_scale)
+    a, _ = gpu_run(torch, lib, w, num_splits=1)
+    w.k_pages = w.k_pages.astype(np.float16)
+    w.v_pages = w.v_pages.astype(np.float16)
+    w.k_scale = w.v_scale = None
+    b, _ = gpu_run(torch, lib, w, num_splits=1)
+    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-5)
+
+
+def test_output_guard_words_untouched(torch, lib):
+    w = generate(SMALL, seed=15)
+    d = to_dev(torch, w)
+    n = w.q.size
+    buf = torch.full((n + 2 * 64,), 12345.0, dtype=torch.float32, device="cuda:0")
+    out = buf[64:64 + n].view(w.q.shape)
+    lib.decode_attn_ex(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
+                       w.scale, out=out, num_splits=3)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:64] == 12345.0) and np.all(host[64 + n:] == 12345.0)
+    assert_parity(host[64:64 + n].reshape(w.q.shape), oracle_run(w)[0], "guarded")
+
+
+def test_library_owned_workspace_entry_point(torch, lib):
+    w = generate(SMALL.with_(len_hi=2000), seed=16)
+    d = to_dev(torch, w)
+    out = lib.decode_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
+                          w.scale)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), oracle_run(w)[0], "decode_attn")
+    ex, _ = gpu_run(torch, lib, w, num_splits=0, lse=False, dev_inputs=d)
+    assert np.array_equal(out.cpu().numpy(), ex)
+
+
+def test_one_hip_runtime_and_native_library(torch, lib):
+    lib.load_library()
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    ours = {ln.split()[-1] for ln in maps if "libdecode_attn.so" in ln}
+    assert len(hip) == 1, f"more than one HIP runtime mapped: {hip}"
+    assert len(ours) == 1 and next(iter(ours)).startswith(os.path.dirname(lib.__file__))
+
+
+# ------------------------------------------------------------------ the preset workloads
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+def test_preset_workload_full_size(torch, lib, index):
+    """Each preset at its full size, in the launch configuration the benchmark times
+    (library-chosen split plan), compared elementwise on every output."""
+    w = generate(CONFIGS[index])
+    print(f"case preset {index} ({CONFIGS[index].name}) pages={w.num_pages}", flush=True)
+    got, lse = gpu_run(torch, lib, w, num_splits=0)
+    ref, ref_lse = oracle_run(w)
+    assert_parity(got, ref, f"preset {index}")
+    assert_lse(lse, ref_lse, "lse")
