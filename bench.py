@@ -1,9 +1,8 @@
 #!/usr/bin/env python3
 """Decode-phase paged attention on one MI355X: KV-read GB/s and us/step.
 
-One step is one decode_attn call over the whole batch (the split kernel, plus
-the merge kernel when the plan has more than one partition): one layer's decode
-attention. The default workload is the Llama-2-7B-shaped MHA batch (batch 48,
+One step is one decode_attn call over the whole batch (the streaming kernel and
+the merge of the (sequence, head) pairs it cut): one layer's decode attention. The default workload is the Llama-2-7B-shaped MHA batch (batch 48,
 32 query = 32 KV heads, head_dim 128, seq_lens uniform in [18, 563], 16-token
 pages in a shuffled pool, fp16 K/V ~ N(0, 1)); --config picks another preset.
 
@@ -49,16 +48,18 @@ def kernel_source_hash() -> str:
 
 
 def read_traffic(workload_name: str):
-    """HBM bytes per launch from the committed counter summary, if it is current."""
-    path = os.path.join(PROFILES, f"decode_split_{workload_name}_pmc.txt")
+    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3 summary
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter reads for a
+    plain copy of known size), or None when there is none or the kernels changed since."""
+    path = os.path.join(PROFILES, f"decode_attn_{workload_name}.txt")
     if not os.path.exists(path):
         return None, "no counter summary"
     fields = {}
     with open(path) as f:
         for line in f:
-            if ":" in line:
+            if ":" in line and not line.startswith((" ", "#")):
                 k, v = line.split(":", 1)
-                fields[k.strip()] = v.strip()
+                fields.setdefault(k.strip(), v.strip())
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
     try:
@@ -123,7 +124,10 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--splits", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="stream mode on this many workgroups (0 = the library's plan)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split mode with this many partitions (0 = the library's plan)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -163,24 +167,25 @@ def main():
     stream = torch.cuda.current_stream(dev)
     kv_type = binding.KV_INT8 if cfg.kv_dtype == "int8" else binding.KV_FP16
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    splits, pps = binding.plan_splits(cfg.batch, cfg.max_blocks_per_seq, cfg.n_kv_heads,
-                                      cfg.block_size, args.splits, num_cus)
+    plan = binding.plan(cfg.batch, cfg.max_blocks_per_seq, cfg.n_q_heads, cfg.n_kv_heads,
+                        cfg.block_size, args.workgroups, args.splits, num_cus)
+    explicit = bool(args.workgroups or args.splits)
 
     # Marshal the arguments once; the timed loop calls the C ABI directly.
     p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
     s_handle = ctypes.c_void_p(stream.cuda_stream)
     call_args = []
     workspace = None
-    if args.splits:
-        need = binding.workspace_size(cfg.batch, cfg.n_q_heads, cfg.head_dim, splits)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if explicit and plan.workspace_bytes:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     for kp, vp, ks, vs in pools:
         common = (p(q), p(kp), p(vp), p(ks), p(vs), p(bt), p(sl), cfg.batch,
                   cfg.max_blocks_per_seq, w.num_pages, cfg.n_q_heads, cfg.n_kv_heads,
                   cfg.head_dim, cfg.block_size, kv_type, float(w.scale), p(out))
-        if args.splits:
-            call_args.append(("ex", common + (None, args.splits, p(workspace),
-                                              workspace.numel(), s_handle)))
+        if explicit:
+            call_args.append(("ex", common + (None, args.workgroups, args.splits, p(workspace),
+                                              ws_bytes, s_handle)))
         else:
             call_args.append(("auto", common + (s_handle,)))
 
@@ -190,35 +195,37 @@ def main():
         if st != 0:
             raise RuntimeError(f"decode_attn failed: {binding.STATUS.get(st, st)}")
 
-    log(f"plan: splits={splits} pages_per_split={pps} replicas={reps} "
+    log(f"plan: {plan} replicas={reps} "
         f"pool={pool_bytes / 1e6:.1f} MB kv_bytes/step={w.kv_bytes / 1e6:.1f} MB")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    begin = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # Timed region: exactly K back-to-back steps between one pair of HIP events recorded
+    # on the launch stream. No event sits between steps: an event record between two
+    # launches delays the second one by several microseconds on this GPU.
     start_ev = torch.cuda.Event(enable_timing=True)
     stop_ev = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start_ev.record(stream)
     for i in range(args.steps):
-        begin[i].record(stream)
         step(args.warmup + i)
-        end[i].record(stream)
     stop_ev.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start_ev.elapsed_time(stop_ev)
-    launch_ms = [b.elapsed_time(e) for b, e in zip(begin, end)]
-    avg_launch_s = float(np.mean(launch_ms)) / 1e3
     ms_per_step = total_ms / args.steps
+    # A step is the main kernel and the merge launched right behind it; back-to-back
+    # launches leave no gap, so the step time is the kernels' summed duration and is taken,
+    # conservatively, as the duration of the dominant (main) launch.
+    avg_launch_s = ms_per_step / 1e3
     gbs = w.kv_bytes * args.steps / (total_ms / 1e3) / 1e9
     achieved = w.kv_bytes / avg_launch_s / 1e9
     log(f"steps={args.steps} total={total_ms:.3f} ms (wall {wall * 1e3:.1f} ms) "
-        f"us/step={ms_per_step * 1e3:.2f} per-launch avg={avg_launch_s * 1e6:.2f} us "
-        f"p50={np.median(launch_ms) * 1e3:.2f} us GB/s={gbs:.1f} ({gbs / HBM_PEAK_GBS:.3f} of peak)")
+        f"us/step={ms_per_step * 1e3:.2f} GB/s={gbs:.1f} ({gbs / HBM_PEAK_GBS:.3f} of peak)")
+    if wall * 1e3 > 1.5 * total_ms:
+        log("warning: host launch rate may be limiting the step rate")
 
     traffic, traffic_src = read_traffic(cfg.name)
     log(f"traffic: {traffic} ({traffic_src})")
@@ -249,7 +256,9 @@ def main():
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "seq_lens": f"uniform [{cfg.len_lo}, {cfg.len_hi}], seed {w.seed}",
             "tokens": int(w.seq_lens.sum()), "num_pages": w.num_pages,
-            "num_splits": splits, "pages_per_split": pps, "replicas": reps,
+            "plan": {"mode": "stream" if plan.mode == binding.MODE_STREAM else "split",
+                     "workgroups": plan.num_workgroups, "splits": plan.num_splits},
+            "replicas": reps,
             "kv_bytes_per_step": int(w.kv_bytes),
         },
         "roofline": {
@@ -259,7 +268,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "split_kernel" + (" + merge_kernel" if splits > 1 else ""),
+            "kernel": ("stream_kernel + piece_merge_kernel" if plan.mode == binding.MODE_STREAM
+                       else "split_kernel" + (" + split_merge_kernel" if plan.num_splits > 1 else ""))
+                      + " (one step)",
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
         },
         "cpu_baseline": baseline,

@@ -32,12 +32,27 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 
+MODE_STREAM = 0
+MODE_SPLIT = 1
+
+
+class Plan(ctypes.Structure):
+    """Mirror of decode_attn_plan_t."""
+    _fields_ = [("mode", _I), ("num_workgroups", _I), ("num_splits", _I),
+                ("pages_per_split", _I), ("workspace_bytes", _SZ)]
+
+    def __repr__(self):
+        mode = "stream" if self.mode == MODE_STREAM else "split"
+        return (f"Plan(mode={mode}, num_workgroups={self.num_workgroups}, "
+                f"num_splits={self.num_splits}, pages_per_split={self.pages_per_split}, "
+                f"workspace_bytes={self.workspace_bytes})")
+
+
 _SIGNATURES = {
     "decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "decode_attn_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
-                            _P, _I, _P, _SZ, _P]),
-    "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
-    "decode_attn_workspace_size": (_SZ, [_I, _I, _I, _I]),
+                            _P, _I, _I, _P, _SZ, _P]),
+    "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
 }
@@ -154,29 +169,29 @@ def decode_attn(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=No
     return out
 
 
-def plan_splits(batch: int, max_blocks_per_seq: int, n_kv_heads: int, block_size: int = 16,
-                requested_splits: int = 0, num_cus: int = 0):
-    """Return (num_splits, pages_per_split) as the library would use them."""
+def plan(batch: int, max_blocks_per_seq: int, n_q_heads: int, n_kv_heads: int,
+         block_size: int = 16, num_workgroups: int = 0, num_splits: int = 0,
+         num_cus: int = 0) -> Plan:
+    """The plan the library uses for these shapes and requests (see decode_attn_plan)."""
     lib = load_library()
-    s, p = _I(0), _I(0)
-    _check(lib.decode_attn_plan(batch, max_blocks_per_seq, n_kv_heads, block_size,
-                                requested_splits, num_cus, ctypes.byref(s), ctypes.byref(p)),
+    out = Plan()
+    _check(lib.decode_attn_plan(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size,
+                                num_workgroups, num_splits, num_cus, ctypes.byref(out)),
            "decode_attn_plan")
-    return s.value, p.value
-
-
-def workspace_size(batch: int, n_q_heads: int, head_dim: int, num_splits: int) -> int:
-    return int(load_library().decode_attn_workspace_size(batch, n_q_heads, head_dim, num_splits))
+    return out
 
 
 def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=None,
-                   v_scale=None, out=None, lse_out=None, num_splits=0, workspace=None):
-    """Decode attention with an explicit split request and caller-owned workspace.
+                   v_scale=None, out=None, lse_out=None, num_workgroups=0, num_splits=0,
+                   workspace=None):
+    """Decode attention with an explicit plan request and caller-owned workspace.
 
-    ``num_splits`` 0 lets the library choose. ``workspace`` (a uint8 device
-    tensor) is allocated here, through torch, when not given. ``lse_out``
-    (fp32 [batch, n_q_heads]) receives the natural-log log-sum-exp of the
-    scores when given. Returns ``out``.
+    ``num_splits`` > 0 asks for split mode with that many page partitions per
+    (sequence, KV head); ``num_workgroups`` > 0 asks for stream mode on that
+    grid; both 0 let the library choose. ``workspace`` (a uint8 device tensor)
+    is allocated here, through torch, when not given. ``lse_out`` (fp32
+    [batch, n_q_heads]) receives the natural-log log-sum-exp of the scores
+    when given. Returns ``out``.
     """
     lib = load_library()
     if out is None:
@@ -188,10 +203,9 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
                 or not lse_out.is_contiguous() or lse_out.device != q.device):
             raise ValueError("lse_out must be contiguous fp32 [batch, n_q_heads] on q's device")
     cus = 0
-    if num_splits == 0:
+    if num_workgroups == 0 and num_splits == 0:
         cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    splits, _ = plan_splits(batch, mb, n_kv, bs, num_splits, cus)
-    need = workspace_size(batch, n_q, d, splits)
+    need = plan(batch, mb, n_q, n_kv, bs, num_workgroups, num_splits, cus).workspace_bytes
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -199,6 +213,7 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
         st = lib.decode_attn_ex(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
                                 _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), batch, mb, np_,
                                 n_q, n_kv, d, bs, kv, float(scale), _ptr(out), _ptr(lse_out),
-                                num_splits, _ptr(workspace), ws_bytes, _stream(q.device))
+                                num_workgroups, num_splits, _ptr(workspace), ws_bytes,
+                                _stream(q.device))
     _check(st, "decode_attn_ex")
     return out

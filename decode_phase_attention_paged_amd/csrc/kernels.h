@@ -8,52 +8,60 @@
 
 namespace dattn {
 
-constexpr int kHeadDim = 128;   // D: elements per (token, head) row
-constexpr int kBlockSize = 16;  // bs: tokens per page
-constexpr int kWaves = 4;       // wavefronts per split workgroup
-constexpr int kSplitThreads = 64 * kWaves;
-constexpr int kMergeThreads = 256;
+constexpr int kHeadDim = 128;     // D: elements per (token, head) row
+constexpr int kBlockSize = 16;    // bs: tokens per page
+constexpr int kWaves = 4;         // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxBatch = 4096;   // sequences whose page counts one workgroup keeps in LDS
+constexpr int kPieceSlots = 2;    // partial results a stream worker can leave
 
 enum class KvType { kF16 = 0, kI8 = 1 };
 
-struct SplitArgs {
-  const void* q;             // fp16 [B, Hq, D]
-  const void* k_pages;       // fp16 | int8 [NP, Hkv, bs, D]
+// How the batch is cut into workgroups.
+//  kStream: a fixed grid of persistent workgroups; the (sequence, KV head, page) units of
+//           the whole batch are dealt out in equal contiguous runs, one per wavefront.
+//  kSplit:  one workgroup per (partition, KV head, sequence) with fixed-size page
+//           partitions; for a few very long caches.
+enum class Mode { kStream = 0, kSplit = 1 };
+
+struct Args {
+  const void* q;               // fp16 [B, Hq, D]
+  const void* k_pages;         // fp16 | int8 [NP, Hkv, bs, D]
   const void* v_pages;
-  const float* k_scale;      // fp32 [NP, Hkv, bs] (int8 only)
+  const float* k_scale;        // fp32 [NP, Hkv, bs] (int8 only)
   const float* v_scale;
   const int32_t* block_table;  // int32 [B, MB]
   const int32_t* seq_lens;     // int32 [B]
-  float* out;                // fp32 [B, Hq, D]          (num_splits == 1)
-  float* lse_out;            // fp32 [B, Hq] or null      (num_splits == 1)
-  float* part_o;             // fp32 [B, Hq, S, D]        (num_splits > 1)
-  float* part_lse;           // fp32 [B, Hq, S], log2 units (num_splits > 1)
+  float* out;                  // fp32 [B, Hq, D]
+  float* lse_out;              // fp32 [B, Hq] or null
+  // Workspace. Stream mode: part_o [workers * kPieceSlots, G, D], part_lse [same rows]
+  // (log2 units), pieces [workers, 4]. Split mode: part_o [B, Hq, S, D], part_lse [B, Hq, S].
+  float* part_o;
+  float* part_lse;
+  int32_t* pieces;
   int batch;
-  int max_blocks;            // MB
-  int num_pages;             // NP
+  int max_blocks;              // MB
+  int num_pages;               // NP
   int n_q_heads;
   int n_kv_heads;
-  int num_splits;            // S
-  int pages_per_split;       // pages per partition
-  float scale_log2;          // softmax scale * log2(e)
+  int num_splits;              // split mode: S
+  int pages_per_split;         // split mode: pages per partition
+  float scale_log2;            // softmax scale * log2(e)
 };
 
-struct MergeArgs {
-  const float* part_o;
-  const float* part_lse;
-  const int32_t* seq_lens;
-  float* out;
-  float* lse_out;
-  int batch;
-  int max_blocks;
-  int n_q_heads;
-  int num_splits;
-  int pages_per_split;
+struct Plan {
+  Mode mode;
+  int num_workgroups;   // grid of the main kernel
+  int num_splits;       // split mode only
+  int pages_per_split;  // split mode only
 };
 
-// Enqueue the split kernel: one workgroup per (partition, KV head, sequence).
-hipError_t launch_split(KvType kv, int group, const SplitArgs& a, hipStream_t stream);
-// Enqueue the merge kernel: one workgroup per (sequence, query head).
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// Bytes of workspace a plan needs.
+size_t workspace_bytes(const Plan& plan, int batch, int n_q_heads, int n_kv_heads);
+// Carve the workspace into the partial-result arrays of Args.
+void bind_workspace(Args& a, const Plan& plan, void* workspace);
+
+// Enqueue the main kernel and the merge of the partial results it leaves.
+hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStream_t stream);
 
 }  // namespace dattn

@@ -1,26 +1,38 @@
 // gfx950 (MI355X, CDNA4) kernels for decode-phase paged attention.
 //
-// Split kernel: one 256-thread workgroup per (partition, KV head, sequence). Each of its
-// four wavefronts streams every fourth page of the partition straight from HBM into
-// VGPRs with 16-byte loads (a (page, head) tile is one contiguous 4 KiB block in fp16,
-// so one wave instruction reads 1 KiB of it with no gaps), scores the tile against all
-// G query heads that share the KV head (GQA, xLLM README optimisation list), and folds
-// the scores into a running max / running sum softmax (the online normaliser of the
-// xLLM README SoftMax operator). Dot products over head_dim finish with DPP row
-// reductions inside each 16-lane (fp16) or 8-lane (int8) token row, so no LDS and no
-// atomics are used in the loop. Waves merge their states through LDS at the end in a
-// fixed order. With one partition the workgroup writes the normalised output; with
-// several it writes a partial (output, log-sum-exp) per partition, and the merge kernel
-// combines them by their log-sum-exp weights (PagedAttention v2 / Flash-Decoding,
-// swiftLLM feature list).
+// A unit is one (sequence b, KV head g, logical page j): the 16 tokens of one KV head in
+// one page, i.e. one K tile and one V tile (4 KiB each in fp16). A segment is the run of
+// units of one (b, g) pair. Every kernel here streams units from HBM straight into VGPRs
+// with 16-byte loads (one wave load covers 1 KiB of a tile with no gaps), keeps several
+// units in flight per wave, scores each tile against all G query heads sharing the KV
+// head (GQA, xLLM README optimisation list), finishes the dot products with DPP reductions
+// inside each token row of 16 lanes (fp16) or 8 lanes (int8), and folds the scores into a
+// running max / running sum softmax per lane row (the online normaliser of the xLLM README
+// SoftMax operator). Segments cut between workers leave partial (output, log-sum-exp)
+// pairs that a second kernel merges by their log-sum-exp weights in a fixed order
+// (PagedAttention v2 / Flash-Decoding, swiftLLM feature list). No atomics anywhere, so a
+// given grid gives bitwise-identical results.
+//
+// Two ways of cutting the batch into work:
+//  * stream mode: a fixed grid of persistent workgroups; units are numbered b-major, then
+//    g, then j, and wavefront w of W takes units [w T / W, (w + 1) T / W) of the T units.
+//    Every wave streams the same number of pages whatever the mix of lengths, so no wave
+//    waits on a long tail. Used when the batch has many segments.
+//  * split mode: one workgroup per (page partition, g, b), its four waves interleaving the
+//    partition's pages and merging in LDS. Used for a few very long caches, where stream
+//    mode would cut each segment into hundreds of pieces.
 //
 // The path is bound by HBM bandwidth: per token and KV head it reads 2 * 128 * 2 bytes
-// (fp16) for 4 * G * 128 flops, far below the VALU or MFMA ridge point, so the kernel
-// spends its effort on keeping enough loads in flight (two pages per wave, software
-// pipelined) rather than on matrix cores.
+// (fp16) for 4 * G * 128 flops, far below the VALU or MFMA ridge point, so the design
+// spends its effort on keeping loads in flight, not on matrix cores. The only vector
+// memory operations inside the streaming loops are the tile loads: page ids come through
+// scalar loads and query rows from LDS, so the compiler can wait for exactly the oldest
+// tile and leave the newer ones in flight.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -30,30 +42,83 @@ namespace {
 constexpr int kWave = 64;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kQLdsBytes = 16384;   // query rows a stream workgroup stages in LDS
+constexpr int kSplitTable = 1024;   // table entries a split workgroup stages in LDS at a time
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
-// Lane geometry. A lane owns one 16-byte chunk of one token row per load instruction:
-// fp16 rows are 256 B = 16 lanes (4 rows per wave load, 4 loads per page), int8 rows are
-// 128 B = 8 lanes (8 rows per wave load, 2 loads per page). Load i of a page covers bytes
-// [i * 1024, i * 1024 + 1024) of the tile, lane l the 16 bytes at l * 16 within it.
+// Lane geometry. A lane owns one 16-byte chunk of one token row per load instruction.
+// fp16: a row is 256 B = 16 lanes; load i of a tile covers tokens 4i .. 4i+3, i.e. the
+//       contiguous bytes [1024 i, 1024 i + 1024), lane l at byte 16 l.
+// int8: a row is 128 B = 8 lanes; lane row r covers tokens 2r and 2r + 1 (loads 0 and 1)
+//       so that its two row scales are one 8-byte load.
 template <KvType kKv>
 struct Geo {
   static constexpr int kElem = kKv == KvType::kF16 ? 2 : 1;
   static constexpr int kChunk = 16 / kElem;                 // elements per lane per load
   static constexpr int kLanesPerRow = kHeadDim / kChunk;    // 16 | 8
-  static constexpr int kRows = kWave / kLanesPerRow;        // token rows per load: 4 | 8
-  static constexpr int kLoads = kBlockSize / kRows;         // loads per page tile: 4 | 2
-  static constexpr int kLoadBytes = kRows * kHeadDim * kElem;   // 1024
+  static constexpr int kRows = kWave / kLanesPerRow;        // lane rows: 4 | 8
+  static constexpr int kLoads = kBlockSize / kRows;         // loads per tile: 4 | 2
   static constexpr int kTileBytes = kBlockSize * kHeadDim * kElem;
   static constexpr bool kScaled = kKv == KvType::kI8;
   static constexpr int kPairs = kChunk / 2;                 // fp16 pairs per lane per load
+
+  __device__ static int offset(int lane, int i) {
+    if constexpr (kKv == KvType::kF16) return i * 1024 + lane * 16;
+    else return (lane / kLanesPerRow) * 256 + i * 128 + (lane % kLanesPerRow) * 16;
+  }
+  __device__ static int token(int row, int i) {
+    if constexpr (kKv == KvType::kF16) return i * kRows + row;
+    else return 2 * row + i;
+  }
 };
 
+// Tuning per kernel, storage type and group size (index log2 G): units kept in flight per
+// wave, and the waves per SIMD the kernel is compiled for (which caps its VGPRs at 512 /
+// waves). A larger group holds more accumulators, so it keeps fewer tiles.
+constexpr int kStreamDepthF16[4] = {4, 4, 3, 2};
+constexpr int kStreamDepthI8[4] = {6, 4, 3, 2};
+constexpr int kStreamWavesF16[4] = {2, 2, 2, 1};
+constexpr int kStreamWavesI8[4] = {2, 2, 1, 1};
+// Split mode comes in two builds: "wide" for one workgroup per (sequence, KV head) over
+// short caches (many workgroups, so occupancy matters), "deep" for a few long partitions
+// per sequence (about one workgroup per CU, so each wave keeps more tiles in flight).
+constexpr int kWideDepthF16[4] = {2, 2, 2, 2};
+constexpr int kWideDepthI8[4] = {3, 3, 2, 2};
+constexpr int kWideWavesF16[4] = {3, 1, 1, 1};
+constexpr int kWideWavesI8[4] = {2, 1, 1, 1};
+constexpr int kDeepDepthF16[4] = {4, 4, 3, 2};
+constexpr int kDeepDepthI8[4] = {6, 4, 3, 2};
+constexpr int kDeepWavesF16[4] = {1, 1, 1, 1};
+constexpr int kDeepWavesI8[4] = {1, 1, 1, 1};
+
+constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
+
+template <KvType kKv, int kGroup>
+constexpr int stream_depth() {
+  return kKv == KvType::kF16 ? kStreamDepthF16[log2_group(kGroup)] : kStreamDepthI8[log2_group(kGroup)];
+}
+template <KvType kKv, int kGroup>
+constexpr int stream_waves() {
+  return kKv == KvType::kF16 ? kStreamWavesF16[log2_group(kGroup)] : kStreamWavesI8[log2_group(kGroup)];
+}
+template <KvType kKv, int kGroup, bool kWide>
+constexpr int split_depth() {
+  constexpr int i = log2_group(kGroup);
+  if constexpr (kWide) return kKv == KvType::kF16 ? kWideDepthF16[i] : kWideDepthI8[i];
+  else return kKv == KvType::kF16 ? kDeepDepthF16[i] : kDeepDepthI8[i];
+}
+template <KvType kKv, int kGroup, bool kWide>
+constexpr int split_waves() {
+  constexpr int i = log2_group(kGroup);
+  if constexpr (kWide) return kKv == KvType::kF16 ? kWideWavesF16[i] : kWideWavesI8[i];
+  else return kKv == KvType::kF16 ? kDeepWavesF16[i] : kDeepWavesI8[i];
+}
+
 // ---------------------------------------------------------------------------------------
-// Cross-lane helpers.
+// Cross-lane and conversion helpers.
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i inside each group of 8
@@ -105,6 +170,25 @@ __device__ __forceinline__ void unpack(const u32x4& raw, h2 (&x)[Geo<kKv>::kPair
   }
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_scalar(const uint32_t* p) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(*p)));
+}
+
+// Read-only scalar load (constant address space: through the scalar cache, counted apart
+// from the vector loads in flight).
+__device__ __forceinline__ int32_t scalar_load(const int32_t* base, size_t idx) {
+  typedef const __attribute__((address_space(4))) int32_t* ConstPtr;
+  return ((ConstPtr)(base))[idx];
+}
+
 // ---------------------------------------------------------------------------------------
 // One page tile of K and V for one KV head, held in VGPRs.
 template <KvType kKv>
@@ -112,37 +196,38 @@ struct Tile {
   using Gm = Geo<kKv>;
   u32x4 k[Gm::kLoads];
   u32x4 v[Gm::kLoads];
-  float ks[Gm::kScaled ? Gm::kLoads : 1];
-  float vs[Gm::kScaled ? Gm::kLoads : 1];
+  float ks[Gm::kScaled ? 2 : 1];
+  float vs[Gm::kScaled ? 2 : 1];
 };
 
+// Tile index = phys * Hkv + g. A unit whose page id failed the range check reads tile 0
+// instead (its output is NaN whatever is read), so every load targets a valid tile.
 template <KvType kKv>
-__device__ __forceinline__ void load_tile(Tile<kKv>& t, const SplitArgs& a, int phys, int g,
+__device__ __forceinline__ void load_tile(Tile<kKv>& t, const Args& a, uint32_t tile_index,
                                           int lane) {
   using Gm = Geo<kKv>;
-  const size_t tile = static_cast<size_t>(phys) * a.n_kv_heads + g;
-  const char* kb = static_cast<const char*>(a.k_pages) + tile * Gm::kTileBytes + lane * 16;
-  const char* vb = static_cast<const char*>(a.v_pages) + tile * Gm::kTileBytes + lane * 16;
+  const size_t base = static_cast<size_t>(tile_index) * Gm::kTileBytes;
+  const char* kb = static_cast<const char*>(a.k_pages) + base;
+  const char* vb = static_cast<const char*>(a.v_pages) + base;
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) {
-    t.k[i] = *reinterpret_cast<const u32x4*>(kb + i * Gm::kLoadBytes);
-    t.v[i] = *reinterpret_cast<const u32x4*>(vb + i * Gm::kLoadBytes);
+    t.k[i] = *reinterpret_cast<const u32x4*>(kb + Gm::offset(lane, i));
+    t.v[i] = *reinterpret_cast<const u32x4*>(vb + Gm::offset(lane, i));
   }
   if constexpr (Gm::kScaled) {
-    const int row = lane / Gm::kLanesPerRow;
-    const float* ksb = a.k_scale + tile * kBlockSize + row;
-    const float* vsb = a.v_scale + tile * kBlockSize + row;
-#pragma unroll
-    for (int i = 0; i < Gm::kLoads; ++i) {
-      t.ks[i] = ksb[i * Gm::kRows];
-      t.vs[i] = vsb[i * Gm::kRows];
-    }
+    const size_t srow = static_cast<size_t>(tile_index) * kBlockSize + 2 * (lane / Gm::kLanesPerRow);
+    const float2 ks = *reinterpret_cast<const float2*>(a.k_scale + srow);
+    const float2 vs = *reinterpret_cast<const float2*>(a.v_scale + srow);
+    t.ks[0] = ks.x;
+    t.ks[1] = ks.y;
+    t.vs[0] = vs.x;
+    t.vs[1] = vs.y;
   }
 }
 
-// Per-lane softmax state for the G query heads of this KV head. All lanes of one token
-// row see the same tokens and hold the same m and l; acc holds this lane's kChunk
-// output columns. Scores are kept in log2 units (scale * log2 e folded in).
+// Per-lane softmax state for the G query heads of one KV head. All lanes of one token row
+// see the same tokens and hold the same m and l; acc holds this lane's kChunk output
+// columns. Scores are kept in log2 units (scale * log2 e folded in).
 template <KvType kKv, int kGroup>
 struct State {
   float m[kGroup];
@@ -150,13 +235,32 @@ struct State {
   float acc[kGroup][Geo<kKv>::kChunk];
 };
 
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void reset(State<kKv, kGroup>& st) {
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) {
+    st.m[h] = kNegInf;
+    st.l[h] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Geo<kKv>::kChunk; ++j) st.acc[h][j] = 0.0f;
+  }
+}
+
+// Query rows of one segment: this lane's kChunk columns of each of the G heads.
+template <KvType kKv, int kGroup>
+using QRegs = h2[kGroup][Geo<kKv>::kPairs];
+
 // Fold one page tile into the running state. With kMasked, tokens at or past `valid`
-// inside the page contribute nothing, whatever their K, V or scale slots hold.
+// inside the page contribute nothing, whatever their K, V or scale slots hold. The tile is
+// only read: masking works on copies.
 template <KvType kKv, int kGroup, bool kMasked>
-__device__ __forceinline__ void consume_tile(Tile<kKv>& t, State<kKv, kGroup>& st,
-                                             const h2 (&qh)[kGroup][Geo<kKv>::kPairs],
-                                             float scale_log2, int row, int valid) {
+__device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGroup>& st,
+                                             const QRegs<kKv, kGroup>& qh, float scale_log2,
+                                             int row, int valid) {
   using Gm = Geo<kKv>;
+  bool ok[Gm::kLoads];
+#pragma unroll
+  for (int i = 0; i < Gm::kLoads; ++i) ok[i] = !kMasked || Gm::token(row, i) < valid;
   float s[kGroup][Gm::kLoads];
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) {
@@ -169,19 +273,8 @@ __device__ __forceinline__ void consume_tile(Tile<kKv>& t, State<kKv, kGroup>& s
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < Gm::kPairs; ++e) d = __builtin_amdgcn_fdot2(kx[e], qh[h][e], d, false);
-      s[h][i] = row_sum<Gm::kLanesPerRow>(d) * f;
-    }
-  }
-  if constexpr (kMasked) {
-#pragma unroll
-    for (int i = 0; i < Gm::kLoads; ++i) {
-      const bool ok = i * Gm::kRows + row < valid;
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) s[h][i] = ok ? s[h][i] : kNegInf;
-      if (!ok) {
-        t.v[i] = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (Gm::kScaled) t.vs[i] = 0.0f;
-      }
+      const float sc = row_sum<Gm::kLanesPerRow>(d) * f;
+      s[h][i] = ok[i] ? sc : kNegInf;
     }
   }
   float p[kGroup][Gm::kLoads];
@@ -206,12 +299,16 @@ __device__ __forceinline__ void consume_tile(Tile<kKv>& t, State<kKv, kGroup>& s
   }
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) {
+    u32x4 raw = t.v[i];
+    if constexpr (kMasked) raw = ok[i] ? raw : u32x4{0u, 0u, 0u, 0u};
     h2 vx[Gm::kPairs];
-    unpack<kKv>(t.v[i], vx);
+    unpack<kKv>(raw, vx);
+    float vscale = 1.0f;
+    if constexpr (Gm::kScaled) vscale = ok[i] ? t.vs[i] : 0.0f;
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       float pw = p[h][i];
-      if constexpr (Gm::kScaled) pw *= t.vs[i];
+      if constexpr (Gm::kScaled) pw *= vscale;
 #pragma unroll
       for (int e = 0; e < Gm::kPairs; ++e) {
         st.acc[h][2 * e] = fmaf(pw, static_cast<float>(vx[e].x), st.acc[h][2 * e]);
@@ -219,6 +316,14 @@ __device__ __forceinline__ void consume_tile(Tile<kKv>& t, State<kKv, kGroup>& s
       }
     }
   }
+}
+
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void consume(const Tile<kKv>& t, State<kKv, kGroup>& st,
+                                        const QRegs<kKv, kGroup>& qh, float scale_log2, int row,
+                                        int valid) {
+  if (valid == kBlockSize) consume_tile<kKv, kGroup, false>(t, st, qh, scale_log2, row, kBlockSize);
+  else consume_tile<kKv, kGroup, true>(t, st, qh, scale_log2, row, valid);
 }
 
 // Merge the (m, l, acc) of the lane `off` away into this lane's, for every head.
@@ -242,16 +347,433 @@ __device__ __forceinline__ void merge_lanes(State<kKv, kGroup>& st, int off) {
   }
 }
 
+// Rows of a wave saw disjoint tokens: merge them so every lane holds the wave's state for
+// its columns.
 template <KvType kKv, int kGroup>
-__global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
+__device__ __forceinline__ void merge_rows(State<kKv, kGroup>& st) {
+#pragma unroll
+  for (int off = Geo<kKv>::kLanesPerRow; off < kWave; off <<= 1) merge_lanes<kKv, kGroup>(st, off);
+}
+
+__device__ __forceinline__ void store_chunk(float* dst, const float* src, int n) {
+  for (int j = 0; j < n; j += 4)
+    *reinterpret_cast<float4*>(dst + j) = make_float4(src[j], src[j + 1], src[j + 2], src[j + 3]);
+}
+
+// Load this lane's columns of the query rows at byte offset `row_off` of q (global).
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void load_query_global(QRegs<kKv, kGroup>& qh, const void* q,
+                                                  size_t row_off, int col) {
   using Gm = Geo<kKv>;
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+    for (int c = 0; c < Gm::kChunk / 8; ++c) {
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(
+          static_cast<const char*>(q) + row_off + h * kHeadDim * 2 + (col * Gm::kChunk + c * 8) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Stream mode. Per sequence the workgroup keeps in LDS its first unit (s_pre) and its
+// page count and last-page fill (s_seq). A wave walks its run with a scalar cursor.
+constexpr uint32_t kFillShift = 24;   // s_seq[b] = pages | (tokens in the last page << 24)
+
+struct Cursor {
+  uint32_t b, g, j;   // sequence, KV head, logical page
+  uint32_t nb;        // pages of sequence b
+  uint32_t fill;      // tokens in its last page (1..16)
+};
+
+// One unit as the streaming loop needs it, all in scalar registers.
+struct Rec {
+  uint32_t tile;   // phys * Hkv + g (0 when the page id failed the range check)
+  uint32_t lin;    // b * Hkv + g: the segment's query rows and output rows start at lin * G
+  uint32_t j, nb;
+  int valid;       // tokens of the page inside the sequence
+  bool ok;         // page id in range
+};
+
+// First unit of worker w, for T units over W workers.
+__device__ __forceinline__ uint32_t unit_begin(uint32_t w, uint32_t total, uint32_t workers) {
+  return static_cast<uint32_t>(static_cast<uint64_t>(w) * total / workers);
+}
+
+// Largest b in [0, batch) with pre[b] <= u, given pre[batch] > u (empty sequences have
+// pre[b] == pre[b + 1] and are skipped).
+__device__ __forceinline__ int find_seq(const uint32_t* pre, int batch, uint32_t u) {
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (lds_scalar(pre + mid) <= u) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void load_seq(Cursor& c, const uint32_t* s_seq) {
+  const uint32_t v = lds_scalar(s_seq + c.b);
+  c.nb = v & ((1u << kFillShift) - 1);
+  c.fill = v >> kFillShift;
+}
+
+__device__ __forceinline__ Cursor cursor_at(const uint32_t* s_pre, const uint32_t* s_seq, int batch,
+                                            uint32_t u) {
+  Cursor c;
+  c.b = static_cast<uint32_t>(find_seq(s_pre, batch, u));
+  load_seq(c, s_seq);
+  const uint32_t r = u - lds_scalar(s_pre + c.b);
+  c.g = r / c.nb;
+  c.j = r - c.g * c.nb;
+  return c;
+}
+
+// Move to the next unit; the caller guarantees there is one.
+__device__ __forceinline__ void advance(Cursor& c, const uint32_t* s_pre, const uint32_t* s_seq,
+                                        uint32_t hkv) {
+  if (++c.j < c.nb) return;
+  c.j = 0;
+  if (++c.g < hkv) return;
+  c.g = 0;
+  do {
+    ++c.b;
+  } while (lds_scalar(s_pre + c.b + 1) == lds_scalar(s_pre + c.b));
+  load_seq(c, s_seq);
+}
+
+__device__ __forceinline__ Rec make_rec(const Cursor& c, int32_t phys, const Args& a, uint32_t hkv) {
+  Rec r;
+  r.ok = static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_pages);
+  r.tile = r.ok ? static_cast<uint32_t>(phys) * hkv + c.g : 0u;
+  r.lin = c.b * hkv + c.g;
+  r.j = c.j;
+  r.nb = c.nb;
+  r.valid = c.j + 1 == c.nb ? static_cast<int>(c.fill) : kBlockSize;
+  return r;
+}
+
+// End of this worker's piece of the segment with rows lin: merge the lane rows, then either
+// write the normalised output (the whole segment was here) or leave the piece in a slot
+// for the merge kernel, recording where all the pieces are if this is the first one.
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void finish_piece(const Args& a, State<kKv, kGroup>& st, uint32_t lin,
+                                             bool seg_first, bool seg_whole, bool seg_bad,
+                                             bool last_page, uint32_t seg_end, uint32_t worker,
+                                             uint32_t workers, uint32_t total_units, int row,
+                                             int col, int lane, int32_t (&record)[4]) {
+  using Gm = Geo<kKv>;
+  merge_rows<kKv, kGroup>(st);
+  const bool complete = last_page && seg_whole;
+  const int slot = static_cast<int>(worker) * kPieceSlots + (seg_first ? 0 : 1);
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) {
+    const float inv = 1.0f / st.l[h];
+    const float lse2 = seg_bad ? nan : st.m[h] + __log2f(st.l[h]);
+    float o[Gm::kChunk];
+#pragma unroll
+    for (int j = 0; j < Gm::kChunk; ++j) o[j] = seg_bad ? nan : st.acc[h][j] * inv;
+    const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
+    if (complete) {
+      if (row == 0) store_chunk(a.out + qrow * kHeadDim + col * Gm::kChunk, o, Gm::kChunk);
+      if (lane == 0 && a.lse_out != nullptr) a.lse_out[qrow] = lse2 * kLn2;
+    } else {
+      const size_t prow = static_cast<size_t>(slot) * kGroup + h;
+      if (row == 0) store_chunk(a.part_o + prow * kHeadDim + col * Gm::kChunk, o, Gm::kChunk);
+      if (lane == 0) a.part_lse[prow] = lse2;
+    }
+  }
+  if (!complete && seg_whole) {
+    // First piece of a segment that continues into later workers; its last piece is in
+    // the last worker w' with unit_begin(w') <= seg_end - 1, i.e. w' = ceil(seg_end W / T) - 1.
+    const uint32_t last_worker = static_cast<uint32_t>(
+        (static_cast<uint64_t>(seg_end) * workers + total_units - 1) / total_units - 1);
+    record[0] = static_cast<int32_t>(lin);
+    record[1] = static_cast<int32_t>(last_worker - worker + 1);
+    record[2] = slot;
+  }
+}
+
+// One wave's run of units [unit_begin(worker), unit_begin(worker + 1)).
+template <KvType kKv, int kGroup, bool kQInLds, int kDepth>
+__device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
+                                           const uint32_t* s_seq, const u32x4* s_q, uint32_t q_lin0,
+                                           uint32_t worker, uint32_t workers, uint32_t total_units,
+                                           int lane) {
+  using Gm = Geo<kKv>;
+  constexpr int kQRowBytes = kGroup * kHeadDim * 2;
+  const int row = lane / Gm::kLanesPerRow;
+  const int col = lane % Gm::kLanesPerRow;
+  const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
+  const uint32_t u0 = unit_begin(worker, total_units, workers);
+  const uint32_t n = unit_begin(worker + 1, total_units, workers) - u0;
+  int32_t record[4] = {0, 0, 0, 0};   // lin, piece count, first slot, unused
+
+  if (n == 0) {
+    // A worker with no units can still sit between two pieces of a cut segment (when
+    // there are fewer units than workers): leave a piece of weight zero in its slot.
+    for (int h = 0; h < kGroup; ++h) {
+      const size_t prow = static_cast<size_t>(worker) * kPieceSlots * kGroup + h;
+      *reinterpret_cast<float2*>(a.part_o + prow * kHeadDim + 2 * lane) = make_float2(0.0f, 0.0f);
+      if (lane == 0) a.part_lse[prow] = kNegInf;
+    }
+  } else {
+    Cursor cur = cursor_at(s_pre, s_seq, a.batch, u0);
+    int32_t phys_next = scalar_load(a.block_table, static_cast<size_t>(cur.b) * a.max_blocks + cur.j);
+    uint32_t taken = 0;   // units whose record has left the cursor
+    // Record of the cursor's unit; then move the cursor on and start the scalar load of
+    // the next page id, which has a whole step to arrive.
+    auto take = [&]() -> Rec {
+      const Rec r = make_rec(cur, phys_next, a, hkv);
+      if (++taken < n) {
+        advance(cur, s_pre, s_seq, hkv);
+        phys_next = scalar_load(a.block_table, static_cast<size_t>(cur.b) * a.max_blocks + cur.j);
+      }
+      return r;
+    };
+
+    Rec rec[kDepth];
+    Tile<kKv> tiles[kDepth];
+    static_for<0, kDepth>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if constexpr (d == 0) rec[0] = take();
+      else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+    });
+
+    State<kKv, kGroup> st;
+    reset(st);
+    QRegs<kKv, kGroup> qh;
+    uint32_t seg_lin = 0;
+    bool seg_first = true;      // the segment is this worker's first
+    bool seg_whole = false;     // the segment started inside this worker (at page 0)
+    bool seg_bad = false;
+
+    auto process = [&](uint32_t k, const Rec& r, const Tile<kKv>& t) {
+      if (k == 0 || r.j == 0) {   // a segment starts: fetch its query rows
+        seg_first = k == 0;
+        seg_whole = r.j == 0;
+        seg_lin = r.lin;
+        seg_bad = false;
+        if constexpr (kQInLds) {
+#pragma unroll
+          for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+            for (int c = 0; c < Gm::kChunk / 8; ++c) {
+              const uint32_t off = (r.lin - q_lin0) * kQRowBytes + h * kHeadDim * 2 +
+                                   (col * Gm::kChunk + c * 8) * 2;
+              const u32x4 raw = s_q[off / 16];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
+            }
+        } else {
+          load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(r.lin) * kQRowBytes, col);
+        }
+      }
+      seg_bad |= !r.ok;
+      consume<kKv, kGroup>(t, st, qh, a.scale_log2, row, r.valid);
+      const bool last_page = r.j + 1 == r.nb;
+      if (last_page || k + 1 == n) {
+        finish_piece<kKv, kGroup>(a, st, seg_lin, seg_first, seg_whole, seg_bad, last_page,
+                                  u0 + k - r.j + r.nb, worker, workers, total_units, row, col,
+                                  lane, record);
+        reset(st);
+      }
+    };
+
+    // Steady state: consume the oldest unit, refill its slot kDepth units ahead. Past the
+    // end of the run a slot re-reads its own tile (a cache hit), so the loads stay
+    // unconditional.
+    uint32_t k0 = 0;
+    for (; k0 + kDepth <= n; k0 += kDepth) {
+      static_for<0, kDepth>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        const uint32_t k = k0 + d;
+        process(k, rec[d], tiles[d]);
+        if (k + kDepth < n) rec[d] = take();
+        load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+      });
+    }
+    static_for<0, kDepth>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if (k0 + d < n) process(k0 + d, rec[d], tiles[d]);
+    });
+  }
+  if (lane == 0) {
+    int32_t* p = a.pieces + static_cast<size_t>(worker) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = record[i];
+  }
+}
+
+template <KvType kKv, int kGroup>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(stream_waves<kKv, kGroup>(), stream_waves<kKv, kGroup>())))
+void stream_kernel(Args a) {
+  __shared__ uint32_t s_pre[kMaxBatch + 1];   // s_pre[b]: first unit of sequence b
+  __shared__ uint32_t s_seq[kMaxBatch];       // pages | last-page fill << 24
+  __shared__ uint32_t s_part[kWaves];
+  __shared__ u32x4 s_q[kQLdsBytes / 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  // The wave index is the same for all 64 lanes; reading it through an SGPR lets the
+  // compiler keep everything derived from it (the unit run, loop bounds) scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int batch = a.batch;
+  const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
+
+  // 1. Exclusive scan of units per sequence (Hkv * pages; 0 for an empty or invalid
+  //    length), 256 sequences per pass.
+  uint32_t carry = 0;
+  for (int base = 0; base < batch; base += kThreads) {
+    const int b = base + tid;
+    uint32_t units = 0;
+    if (b < batch) {
+      const int len = a.seq_lens[b];
+      uint32_t seq = 0;
+      if (len > 0 && len <= a.max_blocks * kBlockSize) {
+        const uint32_t nb = static_cast<uint32_t>((len + kBlockSize - 1) / kBlockSize);
+        units = nb * hkv;
+        seq = nb | (static_cast<uint32_t>(len - static_cast<int>(nb - 1) * kBlockSize) << kFillShift);
+      }
+      s_seq[b] = seq;
+    }
+    uint32_t x = units;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_part[wave] = x;
+    __syncthreads();
+    uint32_t before = carry, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) before += s_part[w];
+      total += s_part[w];
+    }
+    if (b < batch) s_pre[b + 1] = before + x;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) s_pre[0] = 0;
+  __syncthreads();
+  const uint32_t total_units = s_pre[batch];
+
+  // 2. Sequences with no units: zeros for an empty cache, NaN for an invalid length.
+  if (blockIdx.x == 0) {
+    for (int b = tid; b < batch; b += kThreads) {
+      if (s_pre[b + 1] != s_pre[b]) continue;
+      const bool bad = a.seq_lens[b] != 0;
+      const float val = bad ? __builtin_nanf("") : 0.0f;
+      float* o = a.out + static_cast<size_t>(b) * a.n_q_heads * kHeadDim;
+      for (int i = 0; i < a.n_q_heads * kHeadDim; ++i) o[i] = val;
+      if (a.lse_out != nullptr)
+        for (int h = 0; h < a.n_q_heads; ++h)
+          a.lse_out[static_cast<size_t>(b) * a.n_q_heads + h] = bad ? val : kNegInf;
+    }
+  }
+
+  // 3. Stage the query rows of every segment this workgroup touches in LDS, if they fit.
+  //    Segments in unit order are (b, g) pairs in b-major order, which is also the order of
+  //    q in memory ([B, Hkv, G, D]), so they are one contiguous slice.
+  const uint32_t workers = gridDim.x * kWaves;
+  const uint32_t wg_u0 = unit_begin(blockIdx.x * kWaves, total_units, workers);
+  const uint32_t wg_u1 = unit_begin((blockIdx.x + 1) * kWaves, total_units, workers);
+  constexpr int kQRowBytes = kGroup * kHeadDim * 2;
+  uint32_t q_lin0 = 0;
+  bool q_in_lds = false;
+  if (wg_u1 > wg_u0) {
+    const Cursor c0 = cursor_at(s_pre, s_seq, batch, wg_u0);
+    const Cursor c1 = cursor_at(s_pre, s_seq, batch, wg_u1 - 1);
+    q_lin0 = c0.b * hkv + c0.g;
+    const uint32_t bytes = (c1.b * hkv + c1.g - q_lin0 + 1) * kQRowBytes;
+    q_in_lds = bytes <= static_cast<uint32_t>(kQLdsBytes);
+    if (q_in_lds) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) +
+                                                        static_cast<size_t>(q_lin0) * kQRowBytes);
+      for (uint32_t i = tid; i < bytes / 16; i += kThreads) s_q[i] = src[i];
+    }
+  }
+  __syncthreads();
+
+  // 4. This wave's run of units. The query rows come from LDS when the workgroup's slice
+  //    fit, else straight from global memory; the two loops are separate so that the fast
+  //    one never waits on a global query load.
+  const uint32_t worker = blockIdx.x * kWaves + wave;
+  constexpr int kDepth = stream_depth<kKv, kGroup>();
+  if (q_in_lds)
+    run_worker<kKv, kGroup, true, kDepth>(a, s_pre, s_seq, s_q, q_lin0, worker, workers,
+                                          total_units, lane);
+  else
+    run_worker<kKv, kGroup, false, kDepth>(a, s_pre, s_seq, s_q, q_lin0, worker, workers,
+                                           total_units, lane);
+}
+
+// Stream-mode merge: one wave per worker; a worker that recorded a cut segment combines
+// its pieces, piece p living in slot (p == 0 ? first_slot : (worker + p) * kPieceSlots),
+// as sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M) with M = max_p lse_p, in piece order.
+template <int kGroup>
+__global__ __launch_bounds__(kThreads) void piece_merge_kernel(Args a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t worker = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int32_t* rec = a.pieces + static_cast<size_t>(worker) * 4;
+  const int count = scalar_load(rec, 1);
+  if (count <= 0) return;
+  const uint32_t lin = static_cast<uint32_t>(scalar_load(rec, 0));
+  const int first_slot = scalar_load(rec, 2);
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h) {
+    float mx = kNegInf;
+    bool poisoned = false;
+    for (int p = 0; p < count; ++p) {
+      const int slot = p == 0 ? first_slot : static_cast<int>(worker + p) * kPieceSlots;
+      const float v = a.part_lse[static_cast<size_t>(slot) * kGroup + h];
+      poisoned |= v != v;
+      mx = fmaxf(mx, v);
+    }
+    float den = 0.0f, n0 = 0.0f, n1 = 0.0f;
+    for (int p = 0; p < count; ++p) {
+      const int slot = p == 0 ? first_slot : static_cast<int>(worker + p) * kPieceSlots;
+      const size_t prow = static_cast<size_t>(slot) * kGroup + h;
+      const float wgt = fast_exp2(a.part_lse[prow] - mx);
+      const float2 o = *reinterpret_cast<const float2*>(a.part_o + prow * kHeadDim + 2 * lane);
+      den += wgt;
+      n0 += wgt * o.x;
+      n1 += wgt * o.y;
+    }
+    const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
+    const float inv = 1.0f / den;
+    *reinterpret_cast<float2*>(a.out + qrow * kHeadDim + 2 * lane) =
+        poisoned ? make_float2(nan, nan) : make_float2(n0 * inv, n1 * inv);
+    if (lane == 0 && a.lse_out != nullptr) a.lse_out[qrow] = poisoned ? nan : (mx + __log2f(den)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Split mode: one workgroup per (partition s, KV head g, sequence b); wave w streams pages
+// j0 + w, j0 + w + 4, ... of the partition, then the four waves merge through LDS. With
+// one partition the workgroup writes the output; with several it writes a partial result
+// per (b, query head, s) for split_merge_kernel.
+template <KvType kKv, int kGroup, bool kWide>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(split_waves<kKv, kGroup, kWide>(),
+                                   split_waves<kKv, kGroup, kWide>())))
+void split_kernel(Args a) {
+  using Gm = Geo<kKv>;
+  constexpr int kDepth = split_depth<kKv, kGroup, kWide>();
   __shared__ float sm_acc[kWaves][kGroup][kHeadDim];
   __shared__ float sm_m[kWaves][kGroup];
   __shared__ float sm_l[kWaves][kGroup];
   __shared__ int sm_bad[kWaves];
+  __shared__ int32_t s_tab[kSplitTable];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int row = lane / Gm::kLanesPerRow;
   const int col = lane % Gm::kLanesPerRow;
 
@@ -260,8 +782,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
   wg /= a.num_splits;
   const int g = wg % a.n_kv_heads;
   const int b = wg / a.n_kv_heads;
+  const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
 
-  const int seq_len = a.seq_lens[b];
+  const int seq_len = scalar_load(a.seq_lens, b);
   const bool bad_len = seq_len < 0 || seq_len > a.max_blocks * kBlockSize;
   const int nb = bad_len ? 0 : (seq_len + kBlockSize - 1) / kBlockSize;
   const int j0 = split * a.pages_per_split;
@@ -270,70 +793,63 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
   // workgroup still runs to write zeros (empty cache) or NaN (bad length).
   if (a.num_splits > 1 && j0 >= j1) return;
 
-  const int group_base = g * kGroup;
-  h2 qh[kGroup][Gm::kPairs];
-  {
-    const _Float16* qb = static_cast<const _Float16*>(a.q) +
-                         (static_cast<size_t>(b) * a.n_q_heads + group_base) * kHeadDim +
-                         col * Gm::kChunk;
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-#pragma unroll
-      for (int c = 0; c < Gm::kChunk / 8; ++c) {
-        const u32x4 raw = *reinterpret_cast<const u32x4*>(qb + h * kHeadDim + c * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
-      }
-    }
-  }
+  const uint32_t lin = static_cast<uint32_t>(b) * hkv + g;
+  QRegs<kKv, kGroup> qh;
+  load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(lin) * kGroup * kHeadDim * 2, col);
 
   State<kKv, kGroup> st;
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    st.m[h] = kNegInf;
-    st.l[h] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < Gm::kChunk; ++j) st.acc[h][j] = 0.0f;
-  }
-
+  reset(st);
   bool bad = bad_len;
-  const int npages = j1 - j0;
-  const int n_mine = npages > wave ? (npages - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* bt = a.block_table + static_cast<size_t>(b) * a.max_blocks + j0 + wave;
-  for (int k0 = 0; k0 < n_mine && !bad; k0 += kWave) {
-    const int cnt = min(kWave, n_mine - k0);
-    // One table entry per lane for the next (up to) 64 pages of this wave; every entry
-    // is range-checked before any page is touched.
-    const int phys = lane < cnt ? bt[static_cast<size_t>(k0 + lane) * kWaves] : 0;
-    if (__any(lane < cnt && static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_pages))) {
-      bad = true;
-      break;
+  // The partition's table entries go through LDS, kSplitTable pages at a time, so the
+  // streaming loop reads page ids with short LDS loads instead of scalar global loads.
+  const size_t row0 = static_cast<size_t>(b) * a.max_blocks;
+  for (int c0 = j0; c0 < j1; c0 += kSplitTable) {
+    const int c1 = min(c0 + kSplitTable, j1);
+    __syncthreads();   // the previous chunk's entries are no longer read
+    for (int i = threadIdx.x; i < c1 - c0; i += kThreads) s_tab[i] = a.block_table[row0 + c0 + i];
+    __syncthreads();
+    const int npages = c1 - c0;
+    const uint32_t n = npages > wave ? static_cast<uint32_t>((npages - wave + kWaves - 1) / kWaves) : 0u;
+    if (n == 0) continue;
+    // Page k of this wave in the chunk is c0 + wave + 4k.
+    uint32_t taken = 0;
+    auto take = [&]() -> Rec {
+      Rec r;
+      const int i = wave + static_cast<int>(taken) * kWaves;
+      const int32_t phys = static_cast<int32_t>(lds_scalar(reinterpret_cast<const uint32_t*>(s_tab) + i));
+      r.ok = static_cast<unsigned>(phys) < static_cast<unsigned>(a.num_pages);
+      r.tile = r.ok ? static_cast<uint32_t>(phys) * hkv + g : 0u;
+      r.valid = min(kBlockSize, seq_len - (c0 + i) * kBlockSize);
+      ++taken;
+      return r;
+    };
+    Rec rec[kDepth];
+    Tile<kKv> tiles[kDepth];
+    static_for<0, kDepth>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if constexpr (d == 0) rec[0] = take();
+      else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+    });
+    uint32_t k0 = 0;
+    for (; k0 + kDepth <= n; k0 += kDepth) {
+      static_for<0, kDepth>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        bad |= !rec[d].ok;
+        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+        if (k0 + d + kDepth < n) rec[d] = take();
+        load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+      });
     }
-    const int j_last = j0 + wave + (k0 + cnt - 1) * kWaves;
-    const int valid_last = min(kBlockSize, seq_len - j_last * kBlockSize);
-
-    Tile<kKv> ta, tb;
-    load_tile<kKv>(ta, a, __builtin_amdgcn_readlane(phys, 0), g, lane);
-    int k = 0;
-    for (; k + 2 < cnt; k += 2) {
-      load_tile<kKv>(tb, a, __builtin_amdgcn_readlane(phys, k + 1), g, lane);
-      consume_tile<kKv, kGroup, false>(ta, st, qh, a.scale_log2, row, kBlockSize);
-      load_tile<kKv>(ta, a, __builtin_amdgcn_readlane(phys, k + 2), g, lane);
-      consume_tile<kKv, kGroup, false>(tb, st, qh, a.scale_log2, row, kBlockSize);
-    }
-    if (cnt - k == 2) {
-      load_tile<kKv>(tb, a, __builtin_amdgcn_readlane(phys, k + 1), g, lane);
-      consume_tile<kKv, kGroup, false>(ta, st, qh, a.scale_log2, row, kBlockSize);
-      consume_tile<kKv, kGroup, true>(tb, st, qh, a.scale_log2, row, valid_last);
-    } else {
-      consume_tile<kKv, kGroup, true>(ta, st, qh, a.scale_log2, row, valid_last);
-    }
+    static_for<0, kDepth>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if (k0 + d < n) {
+        bad |= !rec[d].ok;
+        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+      }
+    });
   }
-
-  // Rows of this wave saw disjoint tokens: merge them so every lane holds the wave's
-  // state for its columns.
-#pragma unroll
-  for (int off = Gm::kLanesPerRow; off < kWave; off <<= 1) merge_lanes<kKv, kGroup>(st, off);
+  merge_rows<kKv, kGroup>(st);
 
   if (row == 0) {
 #pragma unroll
@@ -355,7 +871,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[w] != 0;
   const float nan = __builtin_nanf("");
-  for (int o = threadIdx.x; o < kGroup * kHeadDim; o += kSplitThreads) {
+  for (int o = threadIdx.x; o < kGroup * kHeadDim; o += kThreads) {
     const int h = o / kHeadDim;
     const int d = o % kHeadDim;
     float mm = kNegInf;
@@ -371,7 +887,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
     }
     const float val = any_bad ? nan : (den > 0.0f ? num / den : 0.0f);
     const float lse2 = any_bad ? nan : (den > 0.0f ? mm + __log2f(den) : kNegInf);
-    const size_t qrow = static_cast<size_t>(b) * a.n_q_heads + group_base + h;
+    const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
     if (a.num_splits == 1) {
       a.out[qrow * kHeadDim + d] = val;
       if (a.lse_out != nullptr && d == 0) a.lse_out[qrow] = lse2 * kLn2;
@@ -383,12 +899,9 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// Merge kernel: one workgroup per (sequence, query head). Partition s holds the
-// normalised partial output o_s and lse_s (log2 units) over its tokens; the result is
-// sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M) with M = max_s lse_s, summed in a fixed
-// order. Only partitions that hold tokens of the sequence are read.
-
+// Split-mode merge: one workgroup per (sequence, query head) over the partitions that hold
+// tokens of the sequence: sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s,
+// reduced in a fixed order.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -400,12 +913,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kMergeParts = kMergeThreads / kHeadDim;   // partition subsets summed apart
+constexpr int kMergeParts = kThreads / kHeadDim;   // partition subsets summed apart
 
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  __shared__ float sm_red[kMergeWaves];
-  __shared__ int sm_nan[kMergeWaves];
+__global__ __launch_bounds__(kThreads) void split_merge_kernel(Args a) {
+  __shared__ float sm_red[kWaves];
+  __shared__ int sm_nan[kWaves];
   __shared__ float sm_part[kMergeParts][kHeadDim];
 
   const int qrow = blockIdx.x;   // b * Hq + h
@@ -421,10 +933,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const float* lse = a.part_lse + static_cast<size_t>(qrow) * a.num_splits;
   const float* po = a.part_o + static_cast<size_t>(qrow) * a.num_splits * kHeadDim;
 
-  // M = max_s lse_s, and whether any partition reported NaN (a bad page).
   float mx = kNegInf;
   int has_nan = 0;
-  for (int s = tid; s < ns; s += kMergeThreads) {
+  for (int s = tid; s < ns; s += kThreads) {
     const float v = lse[s];
     has_nan |= v != v;
     mx = fmaxf(mx, v);
@@ -439,28 +950,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   mx = sm_red[0];
   has_nan = sm_nan[0];
 #pragma unroll
-  for (int w = 1; w < kMergeWaves; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     mx = fmaxf(mx, sm_red[w]);
     has_nan |= sm_nan[w];
   }
   const float base = mx == kNegInf ? 0.0f : mx;
   __syncthreads();
 
-  // Denominator sum_s 2^(lse_s - M), reduced in a fixed tree order.
   float den = 0.0f;
-  for (int s = tid; s < ns; s += kMergeThreads) den += fast_exp2(lse[s] - base);
+  for (int s = tid; s < ns; s += kThreads) den += fast_exp2(lse[s] - base);
   den = wave_sum(den);
   if (lane == 0) sm_red[wave] = den;
   __syncthreads();
   den = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) den += sm_red[w];
+  for (int w = 0; w < kWaves; ++w) den += sm_red[w];
 
-  // Numerator: thread (part, d) sums partitions part, part + kMergeParts, ...
   const int d = tid % kHeadDim;
   const int part = tid / kHeadDim;
   float num = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
   for (int s = part; s < ns; s += kMergeParts)
     num += fast_exp2(lse[s] - base) * po[static_cast<size_t>(s) * kHeadDim + d];
   sm_part[part][d] = num;
@@ -478,35 +987,84 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
 template <KvType kKv, int kGroup>
-hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(a.num_splits) * a.n_kv_heads * a.batch;
-  hipLaunchKernelGGL((split_kernel<kKv, kGroup>), dim3(grid), dim3(kSplitThreads), 0, stream, a);
+hipError_t launch_t(const Args& a, const Plan& plan, hipStream_t stream) {
+  if (plan.mode == Mode::kStream) {
+    hipLaunchKernelGGL((stream_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,
+                       stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((piece_merge_kernel<kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  // One partition per (sequence, KV head) means many short workgroups: the wide build.
+  if (plan.num_splits == 1)
+    hipLaunchKernelGGL((split_kernel<kKv, kGroup, true>), dim3(plan.num_workgroups), dim3(kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((split_kernel<kKv, kGroup, false>), dim3(plan.num_workgroups),
+                       dim3(kThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.num_splits == 1) return err;
+  hipLaunchKernelGGL(split_merge_kernel, dim3(a.batch * a.n_q_heads), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 template <KvType kKv>
-hipError_t launch_split_kv(int group, const SplitArgs& a, hipStream_t stream) {
+hipError_t launch_kv(int group, const Args& a, const Plan& plan, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_split_t<kKv, 1>(a, stream);
-    case 2: return launch_split_t<kKv, 2>(a, stream);
-    case 4: return launch_split_t<kKv, 4>(a, stream);
-    case 8: return launch_split_t<kKv, 8>(a, stream);
+    case 1: return launch_t<kKv, 1>(a, plan, stream);
+    case 2: return launch_t<kKv, 2>(a, plan, stream);
+    case 4: return launch_t<kKv, 4>(a, plan, stream);
+    case 8: return launch_t<kKv, 8>(a, plan, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+constexpr size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
 }  // namespace
 
-hipError_t launch_split(KvType kv, int group, const SplitArgs& a, hipStream_t stream) {
-  return kv == KvType::kF16 ? launch_split_kv<KvType::kF16>(group, a, stream)
-                            : launch_split_kv<KvType::kI8>(group, a, stream);
+size_t workspace_bytes(const Plan& plan, int batch, int n_q_heads, int n_kv_heads) {
+  const size_t group = static_cast<size_t>(n_q_heads / n_kv_heads);
+  if (plan.mode == Mode::kStream) {
+    const size_t workers = static_cast<size_t>(plan.num_workgroups) * kWaves;
+    const size_t rows = workers * kPieceSlots * group;
+    return align256(rows * kHeadDim * sizeof(float)) + align256(rows * sizeof(float)) +
+           align256(workers * 4 * sizeof(int32_t));
+  }
+  if (plan.num_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(batch) * n_q_heads * plan.num_splits;
+  return align256(rows * kHeadDim * sizeof(float)) + align256(rows * sizeof(float));
 }
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(a.batch) * a.n_q_heads;
-  hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(kMergeThreads), 0, stream, a);
-  return hipGetLastError();
+void bind_workspace(Args& a, const Plan& plan, void* workspace) {
+  a.part_o = a.part_lse = nullptr;
+  a.pieces = nullptr;
+  if (workspace == nullptr) return;
+  const size_t group = static_cast<size_t>(a.n_q_heads / a.n_kv_heads);
+  char* p = static_cast<char*>(workspace);
+  if (plan.mode == Mode::kStream) {
+    const size_t workers = static_cast<size_t>(plan.num_workgroups) * kWaves;
+    const size_t rows = workers * kPieceSlots * group;
+    a.part_o = reinterpret_cast<float*>(p);
+    p += align256(rows * kHeadDim * sizeof(float));
+    a.part_lse = reinterpret_cast<float*>(p);
+    p += align256(rows * sizeof(float));
+    a.pieces = reinterpret_cast<int32_t*>(p);
+  } else {
+    const size_t rows = static_cast<size_t>(a.batch) * a.n_q_heads * plan.num_splits;
+    a.part_o = reinterpret_cast<float*>(p);
+    p += align256(rows * kHeadDim * sizeof(float));
+    a.part_lse = reinterpret_cast<float*>(p);
+  }
+}
+
+hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStream_t stream) {
+  return kv == KvType::kF16 ? launch_kv<KvType::kF16>(group, a, plan, stream)
+                            : launch_kv<KvType::kI8>(group, a, plan, stream);
 }
 
 }  // namespace dattn

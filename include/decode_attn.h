@@ -15,25 +15,32 @@
  *     lse[b,h]   = ln sum_t exp(s_t)              (natural log; -inf when L_b = 0)
  *
  * The library reaches this with a single-pass online-normaliser softmax (xLLM README,
- * SoftMax operator) and, for long caches, a split of each sequence into page-aligned
- * partitions whose partial (out, lse) are merged by their log-sum-exp weights
- * (swiftLLM feature list: PagedAttention v2 / Flash-Decoding). Both only change the
- * order of rounding; out is the plain softmax result above.
+ * SoftMax operator) and cuts long caches into pieces whose partial (out, lse) are merged
+ * by their log-sum-exp weights (swiftLLM feature list: PagedAttention v2 /
+ * Flash-Decoding). Two plans cut the batch:
+ *  - stream mode: the (sequence, KV head, page) units of the whole batch are dealt out in
+ *    equal contiguous runs to a fixed grid of persistent workgroups, one run per
+ *    wavefront, so every wave streams the same number of pages whatever the length mix;
+ *  - split mode: one workgroup per (page partition, KV head, sequence), for a few very
+ *    long caches.
+ * Either only changes the order of rounding; out is the plain softmax result above.
  *
  * Memory layout (all row-major and contiguous; all tensor pointers are DEVICE pointers
  * owned by the caller, for example torch tensors; the library never frees them):
  *
- *     q            fp16  [batch, n_q_heads, head_dim]
- *     k_pages      fp16 or int8  [num_pages, n_kv_heads, block_size, head_dim]
+ *     q            fp16  [batch, n_q_heads, head_dim], 16-byte aligned
+ *     k_pages      fp16 or int8  [num_pages, n_kv_heads, block_size, head_dim], 16-byte
+ *                  aligned
  *     v_pages      same type and shape as k_pages
- *     k_scale      fp32  [num_pages, n_kv_heads, block_size]   (INT8 only, else NULL)
- *     v_scale      fp32  [num_pages, n_kv_heads, block_size]   (INT8 only, else NULL)
+ *     k_scale      fp32  [num_pages, n_kv_heads, block_size]   (INT8 only, else NULL;
+ *     v_scale      fp32  [num_pages, n_kv_heads, block_size]    8-byte aligned)
  *     block_table  int32 [batch, max_blocks_per_seq]: entry (b, j) is the physical page
  *                  holding tokens j*block_size .. j*block_size+block_size-1 of sequence b.
  *                  Only entries j < ceil(L_b / block_size) are read; the rest may hold
  *                  anything (for example -1).
  *     seq_lens     int32 [batch]: L_b, with 0 <= L_b <= max_blocks_per_seq * block_size.
- *     out          fp32  [batch, n_q_heads, head_dim]; must not overlap any input.
+ *     out          fp32  [batch, n_q_heads, head_dim], 16-byte aligned; must not overlap
+ *                  any input.
  *     lse_out      fp32  [batch, n_q_heads] or NULL.
  *
  * A (page, KV head) tile is block_size * head_dim contiguous elements (4 KiB in fp16 at
@@ -42,11 +49,14 @@
  * a page past L_b are never used, whatever they hold (NaN included).
  *
  * Supported sizes: head_dim 128, block_size 16, G = n_q_heads / n_kv_heads in
- * {1, 2, 4, 8}. Other values return DECODE_ATTN_ERR_UNSUPPORTED.
+ * {1, 2, 4, 8}, batch * max_blocks_per_seq * n_kv_heads < 2^31 and
+ * num_pages * n_kv_heads < 2^32; stream mode also needs batch <= 4096 (the library's own
+ * plan switches to split mode beyond that). Other values return
+ * DECODE_ATTN_ERR_UNSUPPORTED.
  *
  * Calls are asynchronous: they validate arguments on the host, enqueue kernels on
  * `stream` and return. Nothing is synchronised and no device value is read back; the
- * caller's stream orders the work. The same inputs with the same split count give a
+ * caller's stream orders the work. The same inputs under the same plan give a
  * bitwise-identical out (no atomics; fixed reduction order).
  *
  * Bad device-side values never fault: a sequence whose L_b lies outside
@@ -81,18 +91,33 @@ typedef enum {
   DECODE_ATTN_KV_INT8 = 1 /* per-row INT8 with fp32 row scales (xLLM README, quantisation) */
 } decode_attn_kv_dtype;
 
+/* How a call cuts the batch into work (see the top of this file). */
+typedef enum {
+  DECODE_ATTN_MODE_STREAM = 0,
+  DECODE_ATTN_MODE_SPLIT = 1
+} decode_attn_mode;
+
+/* A plan as decode_attn_plan reports it. */
+typedef struct {
+  int mode;               /* decode_attn_mode */
+  int num_workgroups;     /* grid of the main kernel (256 threads per workgroup) */
+  int num_splits;         /* split mode: partitions per (sequence, KV head); 0 in stream mode */
+  int pages_per_split;    /* split mode: pages per partition; 0 in stream mode */
+  size_t workspace_bytes; /* device workspace decode_attn_ex needs for this plan */
+} decode_attn_plan_t;
+
 /*
  * Decode attention over a paged KV cache (the definition above).
  *
  * batch >= 0 (0 enqueues nothing and returns OK); max_blocks_per_seq >= 1;
  * num_pages >= 1 is the number of pages in each pool, used only to reject bad table
  * entries on the device; scale is the softmax scale (typically 1/sqrt(head_dim)).
- * The split count is chosen by decode_attn_plan for the current device. When it is
- * above 1 the library uses a workspace it owns: one buffer per device, grown with
+ * The plan is the library's choice for the current device (decode_attn_plan with no
+ * request), and the library uses a workspace it owns: one buffer per device, grown with
  * hipMalloc on demand and kept until the process ends. This entry point therefore may
- * allocate, and two calls that overlap on one device (different streams or host
- * threads) must not both need that workspace; such callers use decode_attn_ex.
- * Returns a decode_attn_status.
+ * allocate (on its first call for a shape), and two calls that overlap on one device
+ * (different streams or host threads) must not share that workspace; such callers use
+ * decode_attn_ex. Returns a decode_attn_status.
  */
 int decode_attn(const void* q, const void* k_pages, const void* v_pages,
                 const float* k_scale, const float* v_scale,
@@ -102,34 +127,28 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages,
                 int kv_dtype, float scale, float* out, hipStream_t stream);
 
 /*
- * Split planning (swiftLLM feature list: Flash-Decoding). Each sequence's logical pages
- * [0, max_blocks_per_seq) are cut into *num_splits partitions of *pages_per_split pages;
- * one workgroup handles one (partition, KV head, sequence). requested_splits > 0 asks for
- * that many partitions (the result may be smaller: it is
- * ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits))); 0 lets the
- * library choose from the shape and num_cus (the device's compute-unit count; pass 0 to
- * query the current device, which is the only case that calls HIP). Pure host code
- * otherwise. Returns a decode_attn_status.
+ * Planning (swiftLLM feature list: Flash-Decoding). requested_splits > 0 asks for split
+ * mode with that many page partitions per (sequence, KV head) (the result may be smaller:
+ * it is ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits)));
+ * requested_workgroups > 0 asks for stream mode on that many workgroups; at most one of
+ * the two may be non-zero. With both 0 the library chooses from the shapes and num_cus
+ * (the device's compute-unit count; pass 0 to query the current device, the only case
+ * that calls HIP): split mode when there are fewer (sequence, KV head) pairs than compute
+ * units or more than 4096 sequences, stream mode otherwise. Fills *plan and returns a
+ * decode_attn_status; pure host code apart from the device query.
  */
-int decode_attn_plan(int batch, int max_blocks_per_seq, int n_kv_heads, int block_size,
-                     int requested_splits, int num_cus,
-                     int* num_splits, int* pages_per_split);
+int decode_attn_plan(int batch, int max_blocks_per_seq, int n_q_heads, int n_kv_heads,
+                     int block_size, int requested_workgroups, int requested_splits, int num_cus,
+                     decode_attn_plan_t* plan);
 
 /*
- * Bytes of workspace decode_attn_ex needs for a plan with num_splits partitions
- * (0 when num_splits <= 1). Pure host code; returns 0 for invalid sizes.
- */
-size_t decode_attn_workspace_size(int batch, int n_q_heads, int head_dim, int num_splits);
-
-/*
- * decode_attn with an explicit plan and caller-owned workspace; never allocates.
+ * decode_attn with an explicit plan request and caller-owned workspace; never allocates.
  *
- * requested_splits as in decode_attn_plan (0 = library's choice for the current
- * device). workspace: device memory of at least
- * decode_attn_workspace_size(batch, n_q_heads, head_dim, num_splits) bytes for the
- * resulting plan, 256-byte aligned; it may be NULL when the plan has one partition.
- * Its contents on entry do not matter and on return are unspecified; it must not be in
- * use by another call still running. lse_out (nullable) receives lse[b, h] as defined
+ * requested_workgroups and requested_splits as in decode_attn_plan (both 0 = the
+ * library's choice for the current device). workspace: device memory of at least the
+ * plan's workspace_bytes, 256-byte aligned; it may be NULL when that is 0. Its contents
+ * on entry do not matter and on return are unspecified; it must not be in use by another
+ * call still running. lse_out (nullable, 4-byte aligned) receives lse[b, h] as defined
  * above. Returns a decode_attn_status.
  */
 int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
@@ -138,8 +157,8 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
                    int batch, int max_blocks_per_seq, int num_pages,
                    int n_q_heads, int n_kv_heads, int head_dim, int block_size,
                    int kv_dtype, float scale, float* out, float* lse_out,
-                   int requested_splits, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream);
+                   int requested_workgroups, int requested_splits,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);

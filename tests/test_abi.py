@@ -1,5 +1,6 @@
 """The C ABI on the host: the library loads, exports what include/decode_attn.h
-declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+declares, plans deterministically, and rejects bad arguments before any HIP call
+(no GPU needed)."""
 
 import ctypes
 import os
@@ -12,11 +13,16 @@ HEADER = os.path.join(ROOT, "include", "decode_attn.h")
 
 
 @pytest.fixture(scope="module")
-def lib():
-    from decode_phase_attention_paged_amd import binding
-    if not os.path.exists(binding.LIB_PATH):
+def binding():
+    from decode_phase_attention_paged_amd import binding as b
+    if not os.path.exists(b.LIB_PATH):
         from decode_phase_attention_paged_amd import build
         build.build(verbose=False)
+    return b
+
+
+@pytest.fixture(scope="module")
+def lib(binding):
     return binding.load_library()
 
 
@@ -28,8 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "decode_attn", "decode_attn_ex", "decode_attn_plan", "decode_attn_workspace_size",
-        "decode_attn_status_string", "decode_attn_version"])
+        "decode_attn", "decode_attn_ex", "decode_attn_plan", "decode_attn_status_string",
+        "decode_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -37,8 +43,15 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_plan_struct_matches_the_header(binding):
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} decode_attn_plan_t;", text, re.S).group(1)
+    fields = re.findall(r"^\s*(int|size_t)\s+(\w+);", body, flags=re.M)
+    assert [name for _, name in fields] == [f[0] for f in binding.Plan._fields_]
+
+
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 1
+    assert lib.decode_attn_version() >> 16 == 3
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -60,11 +73,11 @@ def call(lib, **over):
                            a["scale"], a["out"], None)
 
 
-def call_ex(lib, splits, ws, ws_bytes, **over):
+def call_ex(lib, wgs, splits, ws, ws_bytes, **over):
     a = dict(GOOD, **over)
     return lib.decode_attn_ex(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["sl"],
                               a["batch"], a["mb"], a["np_"], a["hq"], a["hkv"], a["d"], a["bs"],
-                              a["kv"], a["scale"], a["out"], None, splits, ws, ws_bytes, None)
+                              a["kv"], a["scale"], a["out"], None, wgs, splits, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -82,6 +95,9 @@ def call_ex(lib, splits, ws, ws_bytes, **over):
     (dict(bt=None), 1),
     (dict(q=A + 8), 1),                # q not 16-byte aligned
     (dict(k=2 * A + 4), 1),            # pages not 16-byte aligned
+    (dict(out=6 * A + 4), 1),          # out not 16-byte aligned
+    (dict(kv=1, ks=7 * A + 4, vs=8 * A), 1),   # int8 row scales not 8-byte aligned
+    (dict(mb=1 << 20, hkv=4096, hq=4096), 2),  # unit count beyond 32 bits
     (dict(batch=-1), 1),
     (dict(mb=0), 1),
     (dict(np_=0), 1),
@@ -92,59 +108,80 @@ def test_host_validation(lib, over, status):
     assert call(lib, **over) == status
 
 
-def test_explicit_workspace_checks(lib):
-    # An explicit split request needs no device query; a missing or short workspace is
-    # refused before anything is enqueued.
-    need = lib.decode_attn_workspace_size(2, 8, 128, 4)
-    assert need == 2 * 8 * 4 * 128 * 4 + 256
-    assert call_ex(lib, 4, None, 0) == 3
-    assert call_ex(lib, 4, 9 * A, need - 1) == 3
-    assert call_ex(lib, 4, 9 * A + 16, need) == 3   # not 256-byte aligned
-    assert call_ex(lib, -1, None, 0) == 1
-    assert call_ex(lib, 4, 9 * A, need, hq=6, hkv=4) == 1
+def plan(lib, binding, batch, mb, hq, hkv, wgs=0, splits=0, cus=256):
+    p = binding.Plan()
+    st = lib.decode_attn_plan(batch, mb, hq, hkv, 16, wgs, splits, cus, ctypes.byref(p))
+    assert st == 0, st
+    return p
 
 
-def plan(lib, batch, mb, hkv, requested=0, cus=256):
-    s, p = ctypes.c_int(0), ctypes.c_int(0)
-    assert lib.decode_attn_plan(batch, mb, hkv, 16, requested, cus, ctypes.byref(s),
-                                ctypes.byref(p)) == 0
-    return s.value, p.value
+def test_explicit_plans_need_no_device_and_check_the_workspace(lib, binding):
+    # Stream mode on 4 workgroups: 16 workers x 2 piece slots x G heads of 129 floats, plus
+    # a 16-byte record per worker, each array 256-byte aligned.
+    p = plan(lib, binding, 2, 8, 8, 2, wgs=4)
+    rows = 16 * 2 * 4
+    assert p.mode == binding.MODE_STREAM and p.num_workgroups == 4
+    assert p.workspace_bytes == rows * 128 * 4 + 512 + 256
+    need = p.workspace_bytes
+    assert call_ex(lib, 4, 0, None, 0) == 3
+    assert call_ex(lib, 4, 0, 9 * A, need - 1) == 3
+    assert call_ex(lib, 4, 0, 9 * A + 16, need) == 3   # not 256-byte aligned
+    assert call_ex(lib, -1, 0, None, 0) == 1
+    assert call_ex(lib, 4, 3, None, 0) == 1            # both requests at once
+    assert call_ex(lib, 4, 0, 9 * A, need, hq=6, hkv=4) == 1
+    # Split mode with 3 partitions of 3 pages: partial rows B x Hq x S.
+    s = plan(lib, binding, 2, 8, 8, 2, splits=3)
+    assert (s.mode, s.num_splits, s.pages_per_split, s.num_workgroups) == (
+        binding.MODE_SPLIT, 3, 3, 3 * 2 * 2)
+    assert s.workspace_bytes == 2 * 8 * 3 * 128 * 4 + 256
+    assert call_ex(lib, 0, 3, 9 * A, s.workspace_bytes - 1) == 3
 
 
-def test_plan_explicit_requests(lib):
-    assert plan(lib, 1, 16, 8, requested=1) == (1, 16)
-    assert plan(lib, 1, 16, 8, requested=3) == (3, 6)
-    assert plan(lib, 1, 16, 8, requested=7) == (6, 3)      # ceil(16 / ceil(16 / 7))
-    assert plan(lib, 1, 16, 8, requested=100) == (16, 1)
-    assert plan(lib, 1, 8192, 8, requested=256) == (256, 32)
+def test_stream_mode_refuses_batches_beyond_the_lds_scan(lib, binding):
+    p = binding.Plan()
+    assert lib.decode_attn_plan(4097, 4, 8, 8, 16, 8, 0, 0, ctypes.byref(p)) == 2
+    auto = plan(lib, binding, 4097, 4, 8, 8)
+    assert auto.mode == binding.MODE_SPLIT
 
 
-def test_plan_covers_every_page_once(lib):
+def test_split_requests_round_to_whole_partitions(lib, binding):
+    got = lambda req: (plan(lib, binding, 1, 16, 8, 8, splits=req).num_splits,
+                       plan(lib, binding, 1, 16, 8, 8, splits=req).pages_per_split)
+    assert got(1) == (1, 16)
+    assert got(3) == (3, 6)
+    assert got(7) == (6, 3)       # ceil(16 / ceil(16 / 7))
+    assert got(100) == (16, 1)
     for mb in (1, 2, 15, 36, 256, 8192):
-        for req in (0, 1, 2, 3, 5, 64):
-            s, p = plan(lib, 3, mb, 4, requested=req)
-            assert s * p >= mb and (s - 1) * p < mb and s >= 1
+        for req in (1, 2, 3, 5, 64):
+            p = plan(lib, binding, 3, mb, 8, 4, splits=req)
+            assert p.num_splits * p.pages_per_split >= mb
+            assert (p.num_splits - 1) * p.pages_per_split < mb
 
 
-def test_plan_auto_for_the_preset_shapes(lib):
-    # (batch, MB, Hkv) of the five preset workloads on a 256-CU device.
-    shapes = {1: (1, 16, 8), 2: (48, 36, 32), 3: (160, 256, 8), 4: (1, 8192, 8), 5: (200, 34, 32)}
-    got = {k: plan(lib, *v) for k, v in shapes.items()}
-    assert got[2][0] == 1 and got[5][0] == 1          # batch x heads fills the GPU
-    assert got[4][0] > 1 and got[3][0] > 1            # long caches are split
-    for k, (b, mb, hkv) in shapes.items():
-        s, p = got[k]
-        assert p <= 64 or s == mb
+def test_auto_plan_for_the_preset_shapes(lib, binding):
+    # (batch, MB, Hq, Hkv) of the five preset workloads on a 256-CU device.
+    p1 = plan(lib, binding, 1, 16, 8, 8)
+    p2 = plan(lib, binding, 48, 36, 32, 32)
+    p3 = plan(lib, binding, 160, 256, 32, 8)
+    p4 = plan(lib, binding, 1, 8192, 32, 8)
+    p5 = plan(lib, binding, 200, 34, 32, 32)
+    # Many (sequence, head) pairs over short caches: one workgroup per pair.
+    for p, b, hkv in ((p2, 48, 32), (p5, 200, 32)):
+        assert (p.mode, p.num_splits, p.num_workgroups) == (binding.MODE_SPLIT, 1, b * hkv)
+        assert p.workspace_bytes == 0
+    # Many pairs over long caches of mixed length: the balanced stream.
+    assert p3.mode == binding.MODE_STREAM and p3.num_workgroups == 512
+    # Few long caches: split mode, about one workgroup per CU.
+    assert (p4.mode, p4.num_splits, p4.pages_per_split, p4.num_workgroups) == (
+        binding.MODE_SPLIT, 32, 256, 256)
+    assert p1.mode == binding.MODE_SPLIT and p1.num_splits == 16
+    assert plan(lib, binding, 160, 256, 32, 8, cus=80).num_workgroups == 160
 
 
-def test_plan_rejects_bad_arguments(lib):
-    s, p = ctypes.c_int(0), ctypes.c_int(0)
-    assert lib.decode_attn_plan(1, 0, 8, 16, 0, 256, ctypes.byref(s), ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 16, -2, 256, ctypes.byref(s), ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 16, 0, 256, None, ctypes.byref(p)) == 1
-
-
-def test_workspace_size_is_zero_without_splits(lib):
-    assert lib.decode_attn_workspace_size(4, 32, 128, 1) == 0
-    assert lib.decode_attn_workspace_size(4, 32, 128, 0) == 0
-    assert lib.decode_attn_workspace_size(0, 32, 128, 8) == 0
+def test_plan_rejects_bad_arguments(lib, binding):
+    p = binding.Plan()
+    assert lib.decode_attn_plan(1, 0, 8, 8, 16, 0, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, -2, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 2, 2, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 6, 4, 16, 0, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 0, 256, None) == 1

@@ -37,12 +37,13 @@ def to_dev(torch, w):
                 v_scale=t(w.v_scale), block_table=t(w.block_table), seq_lens=t(w.seq_lens))
 
 
-def gpu_run(torch, lib, w, num_splits=0, lse=True, dev_inputs=None):
+def gpu_run(torch, lib, w, num_workgroups=0, lse=True, dev_inputs=None, num_splits=0):
     d = dev_inputs or to_dev(torch, w)
     lse_out = torch.empty(w.q.shape[:2], dtype=torch.float32, device="cuda:0") if lse else None
     out = lib.decode_attn_ex(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
                              w.scale, k_scale=d["k_scale"], v_scale=d["v_scale"],
-                             lse_out=lse_out, num_splits=num_splits)
+                             lse_out=lse_out, num_workgroups=num_workgroups,
+                             num_splits=num_splits)
     torch.cuda.synchronize()
     return out.cpu().numpy(), (lse_out.cpu().numpy() if lse else None)
 
@@ -73,29 +74,43 @@ SMALL = Config(0, "small_gqa", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128,
 
 # ------------------------------------------------------------------ small, every kernel variant
 
+# Plans exercised: the library's own, stream mode on several grids (64 workgroups give
+# 256 workers for ~100 units, so most are empty and some sit between the pieces of a cut
+# (sequence, head) pair), and split mode with one and several partitions.
+PLANS = [dict(), dict(num_workgroups=1), dict(num_workgroups=3), dict(num_workgroups=64),
+         dict(num_splits=1), dict(num_splits=3)]
+PLAN_IDS = ["auto", "wg1", "wg3", "wg64", "split1", "split3"]
+
+
 @pytest.mark.parametrize("kv", ["fp16", "int8"])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("splits", [1, 3])
-def test_small_all_variants(torch, lib, kv, group, splits):
+@pytest.mark.parametrize("plan", PLANS, ids=PLAN_IDS)
+def test_small_all_variants(torch, lib, kv, group, plan):
     cfg = SMALL.with_(kv_dtype=kv, n_q_heads=2 * group, n_kv_heads=2)
     w = generate(cfg, seed=100 + group)
-    print(f"case kv={kv} G={group} S={splits} lens={w.seq_lens.tolist()}", flush=True)
+    print(f"case kv={kv} G={group} plan={plan} lens={w.seq_lens.tolist()}", flush=True)
     ref, ref_lse = oracle_run(w)
-    got, lse = gpu_run(torch, lib, w, num_splits=splits)
-    assert_parity(got, ref, f"{kv} G={group} S={splits}")
+    got, lse = gpu_run(torch, lib, w, **plan)
+    assert_parity(got, ref, f"{kv} G={group} {plan}")
     assert_lse(lse, ref_lse, "lse")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 19])
-def test_split_counts_and_determinism(torch, lib, splits):
-    w = generate(SMALL, seed=7)
+@pytest.mark.parametrize("plan", [dict(num_workgroups=n) for n in (1, 2, 3, 7, 19, 64, 300)]
+                         + [dict(num_splits=n) for n in (1, 2, 3, 7, 19, 75)],
+                         ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
+def test_plans_and_determinism(torch, lib, plan):
+    w = generate(SMALL.with_(len_hi=1200), seed=7)
     ref, ref_lse = oracle_run(w)
     d = to_dev(torch, w)
-    a, la = gpu_run(torch, lib, w, num_splits=splits, dev_inputs=d)
-    b, lb = gpu_run(torch, lib, w, num_splits=splits, dev_inputs=d)
-    assert_parity(a, ref, f"S={splits}")
+    a, la = gpu_run(torch, lib, w, dev_inputs=d, **plan)
+    b, lb = gpu_run(torch, lib, w, dev_inputs=d, **plan)
+    assert_parity(a, ref, f"{plan}")
     assert_lse(la, ref_lse, "lse")
-    assert np.array_equal(a, b) and np.array_equal(la, lb), "same inputs, same S: not bitwise equal"
+    assert np.array_equal(a, b) and np.array_equal(la, lb), "same inputs, same plan: not bitwise equal"
+
+
+EDGE_PLANS = [dict(num_workgroups=1), dict(num_workgroups=4), dict(num_workgroups=19),
+              dict(num_workgroups=100), dict(num_splits=1), dict(num_splits=4), dict(num_splits=19)]
 
 
 @pytest.mark.parametrize("kv", ["fp16", "int8"])
@@ -108,17 +123,52 @@ def test_edge_lengths_and_nan_canaries(torch, lib, kv):
     print(f"case edge kv={kv}", flush=True)
     ref, ref_lse = oracle_run(w)
     assert np.isfinite(ref).all()
-    for splits in (1, 4, 19):
-        got, lse = gpu_run(torch, lib, w, num_splits=splits)
-        assert np.isfinite(got).all(), f"S={splits}: a NaN canary leaked into the output"
-        assert_parity(got, ref, f"edge {kv} S={splits}")
+    for plan in EDGE_PLANS:
+        got, lse = gpu_run(torch, lib, w, **plan)
+        assert np.isfinite(got).all(), f"{plan}: a NaN canary leaked into the output"
+        assert_parity(got, ref, f"edge {kv} {plan}")
         assert_lse(lse, ref_lse, "lse")
         assert np.all(got[lens == 0] == 0)
 
 
-def test_page_permutation_is_bitwise_invariant(torch, lib):
+@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2)], ids=["wg2", "split2"])
+def test_all_sequences_empty(torch, lib, plan):
+    cfg = SMALL.with_(len_lo=0, len_hi=40)
+    w = generate(cfg, seed=3, seq_lens=np.zeros(cfg.batch, dtype=np.int32))
+    w.k_pages = np.zeros((1,) + w.k_pages.shape[1:], dtype=np.float16)
+    w.v_pages = w.k_pages.copy()
+    got, lse = gpu_run(torch, lib, w, **plan)
+    assert np.all(got == 0) and np.all(np.isneginf(lse))
+
+
+def test_bad_lengths_and_page_ids_give_nan_not_faults(torch, lib):
+    # The kernels range-check every length and every page id they read; a bad one turns
+    # that sequence's output into NaN and reads nothing through it. Other sequences are
+    # exact.
+    w = generate(SMALL.with_(batch=6, len_hi=400), seed=21)
+    ref, _ = oracle_run(w)
+    mb = SMALL.with_(len_hi=400).max_blocks_per_seq
+    lens = w.seq_lens.copy()
+    lens[1] = mb * 16 + 1          # longer than the table allows
+    lens[4] = -3                   # negative
+    table = w.block_table.copy()
+    nb3 = -(-int(lens[3]) // 16)
+    table[3, nb3 - 1] = w.num_pages        # one past the pool
+    table[5, 0] = -7
+    w.seq_lens, w.block_table = lens, table
+    for plan in (dict(num_workgroups=1), dict(num_workgroups=5), dict(num_workgroups=40),
+                 dict(num_splits=1), dict(num_splits=4)):
+        got, lse = gpu_run(torch, lib, w, **plan)
+        for b in (1, 3, 4, 5):
+            assert np.isnan(got[b]).all() and np.isnan(lse[b]).all(), (plan, b)
+        for b in (0, 2):
+            assert_parity(got[b], ref[b], f"clean sequence {b} {plan}")
+
+
+@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2)], ids=["wg2", "split2"])
+def test_page_permutation_is_bitwise_invariant(torch, lib, plan):
     w = generate(SMALL, seed=12, extra_pages=3)
-    a, _ = gpu_run(torch, lib, w, num_splits=2)
+    a, _ = gpu_run(torch, lib, w, **plan)
     perm = np.random.default_rng(0).permutation(w.num_pages)
     k2 = np.empty_like(w.k_pages)
     v2 = np.empty_like(w.v_pages)
@@ -126,17 +176,17 @@ def test_page_permutation_is_bitwise_invariant(torch, lib):
     v2[perm] = w.v_pages
     w.k_pages, w.v_pages = k2, v2
     w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
-    b, _ = gpu_run(torch, lib, w, num_splits=2)
+    b, _ = gpu_run(torch, lib, w, **plan)
     assert np.array_equal(a, b)
 
 
 def test_gqa_matches_repeated_mha(torch, lib):
     w = generate(SMALL, seed=13)
-    a, _ = gpu_run(torch, lib, w, num_splits=1)
+    a, _ = gpu_run(torch, lib, w, num_workgroups=1)
     group = SMALL.n_q_heads // SMALL.n_kv_heads
     w.k_pages = np.repeat(w.k_pages, group, axis=1)
     w.v_pages = np.repeat(w.v_pages, group, axis=1)
-    b, _ = gpu_run(torch, lib, w, num_splits=1)
+    b, _ = gpu_run(torch, lib, w, num_workgroups=1)
     np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
 
 
@@ -146,11 +196,11 @@ def test_int8_unit_scales_match_fp16_on_same_integers(torch, lib):
     w.scale = 0.001  # raw int8 dot products are ~1e3; keep the softmax soft
     w.k_scale = np.ones_like(w.k_scale)
     w.v_scale = np.ones_like(w.v_scale)
-    a, _ = gpu_run(torch, lib, w, num_splits=1)
+    a, _ = gpu_run(torch, lib, w, num_workgroups=1)
     w.k_pages = w.k_pages.astype(np.float16)
     w.v_pages = w.v_pages.astype(np.float16)
     w.k_scale = w.v_scale = None
-    b, _ = gpu_run(torch, lib, w, num_splits=1)
+    b, _ = gpu_run(torch, lib, w, num_workgroups=1)
     np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-5)
 
 
@@ -161,7 +211,7 @@ def test_output_guard_words_untouched(torch, lib):
     buf = torch.full((n + 2 * 64,), 12345.0, dtype=torch.float32, device="cuda:0")
     out = buf[64:64 + n].view(w.q.shape)
     lib.decode_attn_ex(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
-                       w.scale, out=out, num_splits=3)
+                       w.scale, out=out, num_workgroups=3)
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     assert np.all(host[:64] == 12345.0) and np.all(host[64 + n:] == 12345.0)
@@ -175,7 +225,7 @@ def test_library_owned_workspace_entry_point(torch, lib):
                           w.scale)
     torch.cuda.synchronize()
     assert_parity(out.cpu().numpy(), oracle_run(w)[0], "decode_attn")
-    ex, _ = gpu_run(torch, lib, w, num_splits=0, lse=False, dev_inputs=d)
+    ex, _ = gpu_run(torch, lib, w, num_workgroups=0, lse=False, dev_inputs=d)
     assert np.array_equal(out.cpu().numpy(), ex)
 
 
@@ -193,10 +243,10 @@ def test_one_hip_runtime_and_native_library(torch, lib):
 @pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
 def test_preset_workload_full_size(torch, lib, index):
     """Each preset at its full size, in the launch configuration the benchmark times
-    (library-chosen split plan), compared elementwise on every output."""
+    (library-chosen grid), compared elementwise on every output."""
     w = generate(CONFIGS[index])
     print(f"case preset {index} ({CONFIGS[index].name}) pages={w.num_pages}", flush=True)
-    got, lse = gpu_run(torch, lib, w, num_splits=0)
+    got, lse = gpu_run(torch, lib, w, num_workgroups=0)
     ref, ref_lse = oracle_run(w)
     assert_parity(got, ref, f"preset {index}")
     assert_lse(lse, ref_lse, "lse")
