@@ -118,6 +118,11 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+# Kernels one step launches, by plan mode (stream, split, segment).
+KERNELS = {0: "stream_kernel + piece_merge_kernel", 1: "split_kernel + split_merge_kernel",
+           2: "seg_kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,9 +130,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--workgroups", type=int, default=0,
-                    help="stream mode on this many workgroups (0 = the library's plan)")
+                    help="stream mode on this many workgroups, or the grid of segment mode "
+                         "with --splits 1 (0 = the library's plan)")
     ap.add_argument("--splits", type=int, default=0,
-                    help="split mode with this many partitions (0 = the library's plan)")
+                    help="1 = segment mode, >1 = split mode with this many partitions "
+                         "(0 = the library's plan)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -168,7 +175,7 @@ def main():
     kv_type = binding.KV_INT8 if cfg.kv_dtype == "int8" else binding.KV_FP16
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
     plan = binding.plan(cfg.batch, cfg.max_blocks_per_seq, cfg.n_q_heads, cfg.n_kv_heads,
-                        cfg.block_size, args.workgroups, args.splits, num_cus)
+                        cfg.block_size, cfg.kv_dtype, args.workgroups, args.splits, num_cus)
     explicit = bool(args.workgroups or args.splits)
 
     # Marshal the arguments once; the timed loop calls the C ABI directly.
@@ -177,7 +184,7 @@ def main():
     call_args = []
     workspace = None
     if explicit and plan.workspace_bytes:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel()
     for kp, vp, ks, vs in pools:
         common = (p(q), p(kp), p(vp), p(ks), p(vs), p(bt), p(sl), cfg.batch,
@@ -256,7 +263,7 @@ def main():
             "head_dim": cfg.head_dim, "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "seq_lens": f"uniform [{cfg.len_lo}, {cfg.len_hi}], seed {w.seed}",
             "tokens": int(w.seq_lens.sum()), "num_pages": w.num_pages,
-            "plan": {"mode": "stream" if plan.mode == binding.MODE_STREAM else "split",
+            "plan": {"mode": binding._MODE_NAMES[plan.mode],
                      "workgroups": plan.num_workgroups, "splits": plan.num_splits},
             "replicas": reps,
             "kv_bytes_per_step": int(w.kv_bytes),
@@ -268,9 +275,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": ("stream_kernel + piece_merge_kernel" if plan.mode == binding.MODE_STREAM
-                       else "split_kernel" + (" + split_merge_kernel" if plan.num_splits > 1 else ""))
-                      + " (one step)",
+            "kernel": KERNELS[plan.mode] + " (one step)",
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
         },
         "cpu_baseline": baseline,

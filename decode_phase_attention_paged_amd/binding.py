@@ -34,6 +34,8 @@ _SZ = ctypes.c_size_t
 
 MODE_STREAM = 0
 MODE_SPLIT = 1
+MODE_SEGMENT = 2
+_MODE_NAMES = {MODE_STREAM: "stream", MODE_SPLIT: "split", MODE_SEGMENT: "segment"}
 
 
 class Plan(ctypes.Structure):
@@ -42,7 +44,7 @@ class Plan(ctypes.Structure):
                 ("pages_per_split", _I), ("workspace_bytes", _SZ)]
 
     def __repr__(self):
-        mode = "stream" if self.mode == MODE_STREAM else "split"
+        mode = _MODE_NAMES.get(self.mode, str(self.mode))
         return (f"Plan(mode={mode}, num_workgroups={self.num_workgroups}, "
                 f"num_splits={self.num_splits}, pages_per_split={self.pages_per_split}, "
                 f"workspace_bytes={self.workspace_bytes})")
@@ -52,7 +54,7 @@ _SIGNATURES = {
     "decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "decode_attn_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                             _P, _I, _I, _P, _SZ, _P]),
-    "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
+    "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
 }
@@ -170,13 +172,15 @@ def decode_attn(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=No
 
 
 def plan(batch: int, max_blocks_per_seq: int, n_q_heads: int, n_kv_heads: int,
-         block_size: int = 16, num_workgroups: int = 0, num_splits: int = 0,
-         num_cus: int = 0) -> Plan:
-    """The plan the library uses for these shapes and requests (see decode_attn_plan)."""
+         block_size: int = 16, kv_dtype: str = "fp16", num_workgroups: int = 0,
+         num_splits: int = 0, num_cus: int = 0) -> Plan:
+    """The plan the library uses for these shapes and requests (see decode_attn_plan);
+    kv_dtype is "fp16" or "int8"."""
     lib = load_library()
     out = Plan()
+    kv = {"fp16": 0, "int8": 1}[kv_dtype]
     _check(lib.decode_attn_plan(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size,
-                                num_workgroups, num_splits, num_cus, ctypes.byref(out)),
+                                kv, num_workgroups, num_splits, num_cus, ctypes.byref(out)),
            "decode_attn_plan")
     return out
 
@@ -186,9 +190,10 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
                    workspace=None):
     """Decode attention with an explicit plan request and caller-owned workspace.
 
-    ``num_splits`` > 0 asks for split mode with that many page partitions per
-    (sequence, KV head); ``num_workgroups`` > 0 asks for stream mode on that
-    grid; both 0 let the library choose. ``workspace`` (a uint8 device tensor)
+    ``num_splits`` = 1 asks for segment mode (on ``num_workgroups`` workgroups
+    when that is > 0), ``num_splits`` > 1 for split mode with that many page
+    partitions per (sequence, KV head), ``num_workgroups`` > 0 alone for stream
+    mode on that grid; both 0 let the library choose. ``workspace`` (a uint8 device tensor)
     is allocated here, through torch, when not given. ``lse_out`` (fp32
     [batch, n_q_heads]) receives the natural-log log-sum-exp of the scores
     when given. Returns ``out``.
@@ -202,10 +207,10 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
         if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (batch, n_q)
                 or not lse_out.is_contiguous() or lse_out.device != q.device):
             raise ValueError("lse_out must be contiguous fp32 [batch, n_q_heads] on q's device")
-    cus = 0
-    if num_workgroups == 0 and num_splits == 0:
-        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    need = plan(batch, mb, n_q, n_kv, bs, num_workgroups, num_splits, cus).workspace_bytes
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    need = plan(batch, mb, n_q, n_kv, bs, kv_dtype="int8" if kv == KV_INT8 else "fp16",
+                num_workgroups=num_workgroups, num_splits=num_splits,
+                num_cus=cus).workspace_bytes
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -16,7 +16,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (3 << 16) | 0;
+constexpr int kVersion = (4 << 16) | 0;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -26,9 +26,11 @@ constexpr long long kMinUnitsPerWave = 4;
 // Split mode with several partitions is chosen when the batch has fewer (sequence, KV head)
 // segments than compute units; it then aims at this many workgroups per compute unit.
 constexpr int kSplitWorkgroupsPerCu = 1;
-// Caches of at most this many pages use one split-mode workgroup per (sequence, KV head):
-// the spread of lengths is then too small for the balanced stream to pay for its merge.
+// Segment mode (no merge) is the library's choice when caches are at most this many pages
+// (whole segments are then short enough to balance without cutting them) ...
 constexpr int kShortCachePages = 64;
+// ... or when every workgroup gets at least this many segments, longest first.
+constexpr long long kMinSegmentsPerWorkgroup = 2;
 
 std::mutex g_mutex;
 int g_cus[kMaxDevices];            // compute units per device, 0 = not queried yet
@@ -59,11 +61,37 @@ dattn::Plan split_plan(int batch, int max_blocks, int n_kv_heads, int splits) {
   return p;
 }
 
-// requested_splits > 0: split mode; requested_workgroups > 0: stream mode with that grid;
-// both 0: the library's choice for a device with `cus` compute units.
-dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, int requested_workgroups,
-                      int requested_splits, int cus) {
-  if (requested_splits > 0) return split_plan(batch, max_blocks, n_kv_heads, requested_splits);
+// Segment mode on `workgroups` persistent workgroups, or (0) as many as stay resident on
+// `cus` compute units, but no more than there are segments.
+dattn::Plan segment_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType kv, int group,
+                         int workgroups, int cus) {
+  dattn::Plan p{};
+  p.mode = dattn::Mode::kSegment;
+  p.num_splits = 1;
+  const long long segments = static_cast<long long>(batch) * n_kv_heads;
+  (void)max_blocks;
+  if (workgroups > 0) {
+    p.num_workgroups = workgroups;
+  } else {
+    long long wgs = static_cast<long long>(dattn::seg_waves(kv, group)) * cus;
+    if (wgs > segments) wgs = segments;
+    p.num_workgroups = wgs < 1 ? 1 : static_cast<int>(wgs);
+  }
+  return p;
+}
+
+// requested_splits == 1: segment mode (on requested_workgroups workgroups if > 0);
+// requested_splits > 1: split mode; requested_workgroups > 0 alone: stream mode with that
+// grid; both 0: the library's choice for a device with `cus` compute units.
+dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType kv, int group,
+                      int requested_workgroups, int requested_splits, int cus) {
+  if (requested_splits == 1)
+    return segment_plan(batch, max_blocks, n_kv_heads, kv, group, requested_workgroups, cus);
+  if (requested_splits > 1) {
+    dattn::Plan p = split_plan(batch, max_blocks, n_kv_heads, requested_splits);
+    // A request rounded down to one partition is segment mode.
+    return p.num_splits == 1 ? segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus) : p;
+  }
   dattn::Plan p{};
   p.mode = dattn::Mode::kStream;
   if (requested_workgroups > 0) {
@@ -71,12 +99,22 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, int requested_w
     return p;
   }
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
-  if (segments >= cus && (max_blocks <= kShortCachePages || batch > dattn::kMaxBatch))
-    return split_plan(batch, max_blocks, n_kv_heads, 1);
+  // The segment-mode build for INT8 with G = 8 keeps too many registers live and spills, so
+  // the library's own plan only sends it there when the stream cannot take the batch.
+  const bool seg_spills = kv == dattn::KvType::kI8 && group == 8;
+  const bool seg_ok = !seg_spills || batch > dattn::kMaxBatch;
+  // Segment mode needs a few segments per workgroup to balance whole segments, unless the
+  // caches are short.
+  const long long seg_wgs = static_cast<long long>(dattn::seg_waves(kv, group)) * cus;
+  const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * seg_wgs;
+  if (segments >= cus && seg_ok && (seg_balances || batch > dattn::kMaxBatch))
+    return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   if (segments < cus) {
     const long long want = static_cast<long long>(kSplitWorkgroupsPerCu) * cus;
     const long long splits = segments > 0 ? (want + segments - 1) / segments : 1;
-    return split_plan(batch, max_blocks, n_kv_heads, static_cast<int>(splits < 1 ? 1 : splits));
+    const dattn::Plan sp =
+        split_plan(batch, max_blocks, n_kv_heads, static_cast<int>(splits < 2 ? 2 : splits));
+    return sp.num_splits == 1 ? segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus) : sp;
   }
   const long long max_units = segments * max_blocks;
   long long wgs = static_cast<long long>(kStreamWorkgroupsPerCu) * cus;
@@ -87,13 +125,23 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, int requested_w
   return p;
 }
 
+// Whether make_plan reads the compute-unit count: every plan that ends in segment mode
+// without an explicit grid, and the library's own choice.
+bool plan_needs_cus(int max_blocks, int requested_workgroups, int requested_splits) {
+  return requested_workgroups == 0 && (requested_splits <= 1 || max_blocks == 1);
+}
+
+dattn::KvType kv_of(int kv_dtype) {
+  return kv_dtype == DECODE_ATTN_KV_INT8 ? dattn::KvType::kI8 : dattn::KvType::kF16;
+}
+
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 int validate_shapes(int batch, int max_blocks, int n_q_heads, int n_kv_heads, int block_size,
                     int requested_workgroups, int requested_splits) {
   if (batch < 0 || max_blocks < 1 || n_q_heads < 1 || n_kv_heads < 1 || block_size < 1 ||
       requested_workgroups < 0 || requested_splits < 0 ||
-      (requested_workgroups > 0 && requested_splits > 0))
+      (requested_workgroups > 0 && requested_splits > 1))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (n_q_heads % n_kv_heads != 0) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   return DECODE_ATTN_OK;
@@ -168,17 +216,18 @@ int run(const void* q, const void* k_pages, const void* v_pages, const float* k_
   a.pages_per_split = plan.pages_per_split;
   a.scale_log2 = scale * 1.4426950408889634f;
   dattn::bind_workspace(a, plan, workspace);
-  const dattn::KvType kv = kv_dtype == DECODE_ATTN_KV_INT8 ? dattn::KvType::kI8 : dattn::KvType::kF16;
-  if (dattn::launch(kv, n_q_heads / n_kv_heads, a, plan, stream) != hipSuccess)
+  if (dattn::launch(kv_of(kv_dtype), n_q_heads / n_kv_heads, a, plan, stream) != hipSuccess)
     return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
 
 void export_plan(const dattn::Plan& p, int batch, int n_q_heads, int n_kv_heads,
                  decode_attn_plan_t* out) {
-  out->mode = p.mode == dattn::Mode::kStream ? DECODE_ATTN_MODE_STREAM : DECODE_ATTN_MODE_SPLIT;
+  out->mode = p.mode == dattn::Mode::kStream  ? DECODE_ATTN_MODE_STREAM
+              : p.mode == dattn::Mode::kSplit ? DECODE_ATTN_MODE_SPLIT
+                                              : DECODE_ATTN_MODE_SEGMENT;
   out->num_workgroups = p.num_workgroups;
-  out->num_splits = p.mode == dattn::Mode::kSplit ? p.num_splits : 0;
+  out->num_splits = p.mode == dattn::Mode::kStream ? 0 : p.num_splits;
   out->pages_per_split = p.mode == dattn::Mode::kSplit ? p.pages_per_split : 0;
   out->workspace_bytes = dattn::workspace_bytes(p, batch, n_q_heads, n_kv_heads);
 }
@@ -188,18 +237,21 @@ void export_plan(const dattn::Plan& p, int batch, int n_q_heads, int n_kv_heads,
 extern "C" {
 
 int decode_attn_plan(int batch, int max_blocks_per_seq, int n_q_heads, int n_kv_heads,
-                     int block_size, int requested_workgroups, int requested_splits, int num_cus,
-                     decode_attn_plan_t* plan) {
+                     int block_size, int kv_dtype, int requested_workgroups,
+                     int requested_splits, int num_cus, decode_attn_plan_t* plan) {
   if (plan == nullptr || num_cus < 0) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != DECODE_ATTN_KV_FP16 && kv_dtype != DECODE_ATTN_KV_INT8)
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   int st = validate_shapes(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size,
                            requested_workgroups, requested_splits);
   if (st != DECODE_ATTN_OK) return st;
-  if (requested_workgroups == 0 && requested_splits == 0 && num_cus == 0) {
+  if (num_cus == 0 && plan_needs_cus(max_blocks_per_seq, requested_workgroups, requested_splits)) {
     st = current_device_cus(&num_cus);
     if (st != DECODE_ATTN_OK) return st;
   }
-  const dattn::Plan p = make_plan(batch, max_blocks_per_seq, n_kv_heads, requested_workgroups,
-                                  requested_splits, num_cus);
+  const dattn::Plan p = make_plan(batch, max_blocks_per_seq, n_kv_heads, kv_of(kv_dtype),
+                                  n_q_heads / n_kv_heads, requested_workgroups, requested_splits,
+                                  num_cus);
   st = validate_plan(p, batch);
   if (st != DECODE_ATTN_OK) return st;
   export_plan(p, batch, n_q_heads, n_kv_heads, plan);
@@ -218,11 +270,12 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages, cons
   if (st != DECODE_ATTN_OK) return st;
   if (batch == 0) return DECODE_ATTN_OK;
   int cus = 0;
-  if (requested_workgroups == 0 && requested_splits == 0) {
+  if (plan_needs_cus(max_blocks_per_seq, requested_workgroups, requested_splits)) {
     st = current_device_cus(&cus);
     if (st != DECODE_ATTN_OK) return st;
   }
-  const dattn::Plan plan = make_plan(batch, max_blocks_per_seq, n_kv_heads, requested_workgroups,
+  const dattn::Plan plan = make_plan(batch, max_blocks_per_seq, n_kv_heads, kv_of(kv_dtype),
+                                     n_q_heads / n_kv_heads, requested_workgroups,
                                      requested_splits, cus);
   st = validate_plan(plan, batch);
   if (st != DECODE_ATTN_OK) return st;
@@ -247,7 +300,8 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages, const f
   int cus = 0;
   st = current_device_cus(&cus);
   if (st != DECODE_ATTN_OK) return st;
-  const dattn::Plan plan = make_plan(batch, max_blocks_per_seq, n_kv_heads, 0, 0, cus);
+  const dattn::Plan plan = make_plan(batch, max_blocks_per_seq, n_kv_heads, kv_of(kv_dtype),
+                                     n_q_heads / n_kv_heads, 0, 0, cus);
   st = validate_plan(plan, batch);
   if (st != DECODE_ATTN_OK) return st;
   const size_t need = dattn::workspace_bytes(plan, batch, n_q_heads, n_kv_heads);

@@ -15,14 +15,28 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxBatch = 4096;   // sequences whose page counts one workgroup keeps in LDS
 constexpr int kPieceSlots = 2;    // partial results a stream worker can leave
 
+constexpr int kOrderMax = kThreads;  // batches up to this size run longest sequence first
+
 enum class KvType { kF16 = 0, kI8 = 1 };
 
 // How the batch is cut into workgroups.
-//  kStream: a fixed grid of persistent workgroups; the (sequence, KV head, page) units of
-//           the whole batch are dealt out in equal contiguous runs, one per wavefront.
-//  kSplit:  one workgroup per (partition, KV head, sequence) with fixed-size page
-//           partitions; for a few very long caches.
-enum class Mode { kStream = 0, kSplit = 1 };
+//  kStream:  a fixed grid of persistent workgroups; the (sequence, KV head, page) units of
+//            the whole batch are dealt out in equal contiguous runs, one per wavefront.
+//  kSplit:   one workgroup per (partition, KV head, sequence) with fixed-size page
+//            partitions (at least two); for a few very long caches.
+//  kSegment: a fixed grid of persistent workgroups, each taking whole (sequence, KV head)
+//            segments, longest sequences first; no partial results.
+enum class Mode { kStream = 0, kSplit = 1, kSegment = 2 };
+
+constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
+
+// Waves per SIMD the segment-mode kernel is compiled for, by storage type and log2 G; the
+// host sizes that mode's grid to this many workgroups per compute unit.
+constexpr int kSegWavesF16[4] = {3, 2, 2, 1};
+constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
+constexpr int seg_waves(KvType kv, int group) {
+  return kv == KvType::kF16 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];
+}
 
 struct Args {
   const void* q;               // fp16 [B, Hq, D]
@@ -36,6 +50,7 @@ struct Args {
   float* lse_out;              // fp32 [B, Hq] or null
   // Workspace. Stream mode: part_o [workers * kPieceSlots, G, D], part_lse [same rows]
   // (log2 units), pieces [workers, 4]. Split mode: part_o [B, Hq, S, D], part_lse [B, Hq, S].
+  // Segment mode: none.
   float* part_o;
   float* part_lse;
   int32_t* pieces;

@@ -82,19 +82,16 @@ constexpr int kStreamDepthF16[4] = {4, 4, 3, 2};
 constexpr int kStreamDepthI8[4] = {6, 4, 3, 2};
 constexpr int kStreamWavesF16[4] = {2, 2, 2, 1};
 constexpr int kStreamWavesI8[4] = {2, 2, 1, 1};
-// Split mode comes in two builds: "wide" for one workgroup per (sequence, KV head) over
-// short caches (many workgroups, so occupancy matters), "deep" for a few long partitions
-// per sequence (about one workgroup per CU, so each wave keeps more tiles in flight).
-constexpr int kWideDepthF16[4] = {2, 2, 2, 2};
-constexpr int kWideDepthI8[4] = {3, 3, 2, 2};
-constexpr int kWideWavesF16[4] = {3, 1, 1, 1};
-constexpr int kWideWavesI8[4] = {2, 1, 1, 1};
-constexpr int kDeepDepthF16[4] = {4, 4, 3, 2};
-constexpr int kDeepDepthI8[4] = {6, 4, 3, 2};
-constexpr int kDeepWavesF16[4] = {1, 1, 1, 1};
-constexpr int kDeepWavesI8[4] = {1, 1, 1, 1};
+// Split mode runs a few long partitions per sequence, about one workgroup per CU, so each
+// wave keeps many tiles in flight.
+constexpr int kSplitDepthF16[4] = {4, 4, 3, 2};
+constexpr int kSplitDepthI8[4] = {6, 4, 3, 2};
+constexpr int kSplitWavesF16[4] = {1, 1, 1, 1};
+constexpr int kSplitWavesI8[4] = {1, 1, 1, 1};
+// Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
+constexpr int kSegDepthF16[4] = {2, 2, 2, 2};
+constexpr int kSegDepthI8[4] = {1, 3, 2, 1};
 
-constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
 template <KvType kKv, int kGroup>
 constexpr int stream_depth() {
@@ -104,17 +101,17 @@ template <KvType kKv, int kGroup>
 constexpr int stream_waves() {
   return kKv == KvType::kF16 ? kStreamWavesF16[log2_group(kGroup)] : kStreamWavesI8[log2_group(kGroup)];
 }
-template <KvType kKv, int kGroup, bool kWide>
+template <KvType kKv, int kGroup>
 constexpr int split_depth() {
-  constexpr int i = log2_group(kGroup);
-  if constexpr (kWide) return kKv == KvType::kF16 ? kWideDepthF16[i] : kWideDepthI8[i];
-  else return kKv == KvType::kF16 ? kDeepDepthF16[i] : kDeepDepthI8[i];
+  return kKv == KvType::kF16 ? kSplitDepthF16[log2_group(kGroup)] : kSplitDepthI8[log2_group(kGroup)];
 }
-template <KvType kKv, int kGroup, bool kWide>
+template <KvType kKv, int kGroup>
 constexpr int split_waves() {
-  constexpr int i = log2_group(kGroup);
-  if constexpr (kWide) return kKv == KvType::kF16 ? kWideWavesF16[i] : kWideWavesI8[i];
-  else return kKv == KvType::kF16 ? kDeepWavesF16[i] : kDeepWavesI8[i];
+  return kKv == KvType::kF16 ? kSplitWavesF16[log2_group(kGroup)] : kSplitWavesI8[log2_group(kGroup)];
+}
+template <KvType kKv, int kGroup>
+constexpr int seg_depth() {
+  return kKv == KvType::kF16 ? kSegDepthF16[log2_group(kGroup)] : kSegDepthI8[log2_group(kGroup)];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -755,17 +752,335 @@ __global__ __launch_bounds__(kThreads) void piece_merge_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Split mode: one workgroup per (partition s, KV head g, sequence b); wave w streams pages
-// j0 + w, j0 + w + 4, ... of the partition, then the four waves merge through LDS. With
-// one partition the workgroup writes the output; with several it writes a partial result
-// per (b, query head, s) for split_merge_kernel.
-template <KvType kKv, int kGroup, bool kWide>
+// Segment mode: a fixed grid of P persistent workgroups, each taking whole segments (all
+// pages of one (sequence, KV head) pair). Segments are listed rank-major, then by KV head,
+// where rank orders the sequences by decreasing length when the batch has at most
+// kOrderMax of them (ties by index; every workgroup ranks the lengths itself, the same
+// way) and by index otherwise. The list is dealt out in a snake: in round r workgroup w
+// takes position r P + w, or r P + P - 1 - w when r is odd, so the longest segments start
+// first and each workgroup's total stays close to the mean. The four waves of a workgroup
+// interleave the pages of its current segment; each wave keeps one pipeline of tile loads
+// running across segment boundaries. At the end of every segment the waves merge their
+// states through LDS after one barrier; the barrier waits for LDS traffic only, so the
+// tile loads already issued for the next segments stay in flight.
+constexpr int kSegQBytes = 16384;   // query rows of the segments staged in LDS at a time
+
+struct SegInfo {
+  uint32_t b, g;
+  int len;       // tokens, as passed
+  uint32_t nb;   // pages; 0 for an empty cache or an invalid length
+  bool bad;      // invalid length
+};
+
+struct SegList {
+  uint32_t w, P, n, hkv;
+  int max_tokens;
+  bool ordered, lens_in_lds;
+  const uint32_t* order;      // LDS: sequence of each rank
+  const uint32_t* lens;       // LDS: lengths, when lens_in_lds
+  const int32_t* seq_lens;    // global
+
+  // Position in the list of this workgroup's k-th segment.
+  __device__ __forceinline__ uint32_t index(uint32_t k) const {
+    return k * P + ((k & 1u) != 0u ? P - 1u - w : w);
+  }
+  // Sequence and KV head of the k-th segment; with kUniform the caller guarantees k is the
+  // same in all lanes and the lookups go through scalar registers.
+  template <bool kUniform>
+  __device__ __forceinline__ void head_of(uint32_t k, uint32_t& b, uint32_t& g) const {
+    const uint32_t i = index(k);
+    uint32_t rank = i / hkv;
+    // The division runs on the vector unit; bring a uniform result back to a scalar
+    // register so that the loads it addresses stay scalar.
+    if constexpr (kUniform) rank = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(rank)));
+    g = i - rank * hkv;
+    if (!ordered) b = rank;
+    else if constexpr (kUniform) b = lds_scalar(order + rank);
+    else b = order[rank];
+  }
+  __device__ __forceinline__ SegInfo info(uint32_t k) const {
+    SegInfo s;
+    head_of<true>(k, s.b, s.g);
+    s.len = lens_in_lds ? static_cast<int>(lds_scalar(lens + s.b)) : scalar_load(seq_lens, s.b);
+    s.bad = s.len < 0 || s.len > max_tokens;
+    s.nb = s.bad ? 0u : static_cast<uint32_t>((s.len + kBlockSize - 1) / kBlockSize);
+    return s;
+  }
+};
+
+// One unit of a wave's run, all in scalar registers.
+struct SegRec {
+  uint32_t tile;   // phys * Hkv + g (0 when the page id failed the range check)
+  uint32_t k;      // segment index in the workgroup's list; n once the run is over
+  int valid;       // tokens of the page inside the sequence
+  bool ok;         // page id in range
+  bool live;       // false past the end of the run (the slot re-reads an earlier tile)
+};
+
+template <KvType kKv, int kGroup>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(split_waves<kKv, kGroup, kWide>(),
-                                   split_waves<kKv, kGroup, kWide>())))
+__attribute__((amdgpu_waves_per_eu(seg_waves(kKv, kGroup), seg_waves(kKv, kGroup))))
+void seg_kernel(Args a) {
+  using Gm = Geo<kKv>;
+  constexpr int kDepth = seg_depth<kKv, kGroup>();
+  constexpr uint32_t kQRow16 = kGroup * kHeadDim * 2 / 16;   // 16-byte words per segment's queries
+  constexpr uint32_t kChunk = kSegQBytes / (kQRow16 * 16);  // segments per staged chunk
+  __shared__ uint32_t s_len[kMaxBatch];
+  __shared__ int4 s_key[kOrderMax / 4];
+  __shared__ uint32_t s_order[kOrderMax];
+  __shared__ u32x4 s_q[kSegQBytes / 16];
+  __shared__ float sm_acc[2][kWaves][kGroup][kHeadDim];
+  __shared__ float sm_m[2][kWaves][kGroup];
+  __shared__ float sm_l[2][kWaves][kGroup];
+  __shared__ int sm_bad[2][kWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int row = lane / Gm::kLanesPerRow;
+  const int col = lane % Gm::kLanesPerRow;
+  const int batch = a.batch;
+  const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
+
+  SegList L;
+  L.w = blockIdx.x;
+  L.P = gridDim.x;
+  L.hkv = hkv;
+  L.max_tokens = a.max_blocks * kBlockSize;
+  L.ordered = batch <= kOrderMax;
+  L.lens_in_lds = batch <= kMaxBatch;
+  L.order = s_order;
+  L.lens = s_len;
+  L.seq_lens = a.seq_lens;
+  {
+    const uint32_t total = static_cast<uint32_t>(batch) * hkv;
+    const uint32_t full = total / L.P;
+    const uint32_t rem = total - full * L.P;
+    const uint32_t last = (full & 1u) != 0u ? L.P - 1u - L.w : L.w;
+    L.n = full + (last < rem ? 1u : 0u);
+  }
+
+  // 1. Lengths into LDS; rank the sequences by decreasing length (empty and invalid
+  //    lengths count as 0, so they come last).
+  if (L.lens_in_lds)
+    for (int b = tid; b < batch; b += kThreads) s_len[b] = static_cast<uint32_t>(a.seq_lens[b]);
+  if (L.ordered) {
+    int key = -1;   // pads past the batch: below every real key
+    if (tid < batch) {
+      const int len = a.seq_lens[tid];
+      key = len > 0 && len <= L.max_tokens ? len : 0;
+    }
+    reinterpret_cast<int*>(s_key)[tid] = key;
+    __syncthreads();
+    if (tid < batch) {
+      int rank = 0;
+      for (int u4 = 0; u4 < (batch + 3) / 4; ++u4) {
+        const int4 k = s_key[u4];
+        const int u = 4 * u4;
+        rank += (k.x > key || (k.x == key && u < tid)) + (k.y > key || (k.y == key && u + 1 < tid)) +
+                (k.z > key || (k.z == key && u + 2 < tid)) + (k.w > key || (k.w == key && u + 3 < tid));
+      }
+      s_order[rank] = static_cast<uint32_t>(tid);
+    }
+  }
+  __syncthreads();
+  if (L.n == 0) return;   // more workgroups than segments (same for the whole workgroup)
+
+  // 2. Query rows of segments [k0, k0 + kChunk) go to LDS: each thread loads at most
+  //    kQPerThread 16-byte words of them into registers, then stores them.
+  constexpr int kQPerThread = kSegQBytes / 16 / kThreads;
+  const u32x4* q16 = static_cast<const u32x4*>(a.q);
+  u32x4 qbuf[kQPerThread];
+  auto stage_load = [&](uint32_t k0) __attribute__((always_inline)) {
+    const uint32_t words = min(kChunk, L.n - k0) * kQRow16;
+#pragma unroll
+    for (int i = 0; i < kQPerThread; ++i) {
+      const uint32_t idx = static_cast<uint32_t>(tid + i * kThreads);
+      if (idx < words) {
+        const uint32_t t = idx / kQRow16;
+        uint32_t b, g;
+        L.head_of<false>(k0 + t, b, g);
+        qbuf[i] = q16[static_cast<size_t>(b * hkv + g) * kQRow16 + (idx - t * kQRow16)];
+      }
+    }
+  };
+  auto stage_store = [&](uint32_t k0) __attribute__((always_inline)) {
+    const uint32_t words = min(kChunk, L.n - k0) * kQRow16;
+#pragma unroll
+    for (int i = 0; i < kQPerThread; ++i) {
+      const uint32_t idx = static_cast<uint32_t>(tid + i * kThreads);
+      if (idx < words) s_q[idx] = qbuf[i];
+    }
+  };
+  auto stage = [&](uint32_t k0) __attribute__((always_inline)) {
+    stage_load(k0);
+    stage_store(k0);
+  };
+  // The first chunk's loads are issued now and stored to LDS only after the first tile
+  // loads below have been issued, so their latencies overlap.
+  stage_load(0);
+
+  QRegs<kKv, kGroup> qh;
+  auto load_q = [&](uint32_t k) __attribute__((always_inline)) {
+    const uint32_t base = (k % kChunk) * kQRow16 * 16;
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+      for (int c = 0; c < Gm::kChunk / 8; ++c) {
+        const u32x4 raw = s_q[(base + h * kHeadDim * 2 + (col * Gm::kChunk + c * 8) * 2) / 16];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
+      }
+  };
+
+  // 3. This wave's cursor: segment k, page j (j = wave, wave + 4, ...), skipping segments
+  //    too short to give this wave a page.
+  uint32_t ck = 0, cj = 0, cnb = 0, cb = 0, cg = 0;
+  int clen = 0;
+  auto seek = [&]() __attribute__((always_inline)) {
+    for (; ck < L.n; ++ck) {
+      const SegInfo s = L.info(ck);
+      if (static_cast<uint32_t>(wave) < s.nb) {
+        cj = static_cast<uint32_t>(wave);
+        cnb = s.nb;
+        cb = s.b;
+        cg = s.g;
+        clen = s.len;
+        return;
+      }
+    }
+  };
+  seek();
+  int32_t phys_next = ck < L.n ? scalar_load(a.block_table, static_cast<size_t>(cb) * a.max_blocks + cj) : 0;
+  uint32_t last_tile = 0;
+  auto take = [&]() __attribute__((always_inline)) -> SegRec {
+    SegRec r;
+    if (ck >= L.n) {
+      r.live = false;
+      r.ok = true;
+      r.k = L.n;
+      r.tile = last_tile;
+      r.valid = 0;
+      return r;
+    }
+    r.live = true;
+    r.ok = static_cast<unsigned>(phys_next) < static_cast<unsigned>(a.num_pages);
+    r.tile = r.ok ? static_cast<uint32_t>(phys_next) * hkv + cg : 0u;
+    r.k = ck;
+    r.valid = cj + 1 == cnb ? clen - static_cast<int>(cnb - 1) * kBlockSize : kBlockSize;
+    last_tile = r.tile;
+    cj += kWaves;
+    if (cj >= cnb) {
+      ++ck;
+      seek();
+    }
+    if (ck < L.n) phys_next = scalar_load(a.block_table, static_cast<size_t>(cb) * a.max_blocks + cj);
+    return r;
+  };
+
+  SegRec rec[kDepth];
+  Tile<kKv> tiles[kDepth];
+  static_for<0, kDepth>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    rec[d] = take();
+    load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+  });
+  stage_store(0);
+  __syncthreads();
+
+  State<kKv, kGroup> st;
+  reset(st);
+  load_q(0);
+  bool seg_bad = false;
+  uint32_t cur = 0;   // segment whose state st holds
+
+  // End of segment k for this wave: publish the wave's state, meet the other waves, merge
+  // the four states into the output, and stage the next chunk of query rows when k + 1
+  // starts one. Every wave calls this exactly once per segment, in order, so the barriers
+  // pair up.
+  auto finish = [&](uint32_t k) __attribute__((always_inline)) {
+    merge_rows<kKv, kGroup>(st);
+    const uint32_t slot = k & 1u;
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int j = 0; j < Gm::kChunk; ++j) sm_acc[slot][wave][h][col * Gm::kChunk + j] = st.acc[h][j];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        sm_m[slot][wave][h] = st.m[h];
+        sm_l[slot][wave][h] = st.l[h];
+      }
+      sm_bad[slot][wave] = seg_bad ? 1 : 0;
+    }
+    __syncthreads();
+    const SegInfo s = L.info(k);
+    bool any_bad = s.bad;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[slot][w] != 0;
+    const uint32_t lin = s.b * hkv + s.g;
+    const float nan = __builtin_nanf("");
+    for (int o = tid; o < kGroup * kHeadDim; o += kThreads) {
+      const int h = o / kHeadDim;
+      const int d = o % kHeadDim;
+      float mm = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[slot][w][h]);
+      const float base = mm == kNegInf ? 0.0f : mm;
+      float num = 0.0f, den = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float e = fast_exp2(sm_m[slot][w][h] - base);
+        num += e * sm_acc[slot][w][h][d];
+        den += e * sm_l[slot][w][h];
+      }
+      const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
+      a.out[qrow * kHeadDim + d] = any_bad ? nan : (den > 0.0f ? num / den : 0.0f);
+      if (a.lse_out != nullptr && d == 0)
+        a.lse_out[qrow] = any_bad ? nan : (den > 0.0f ? (mm + __log2f(den)) * kLn2 : kNegInf);
+    }
+    if (k + 1 < L.n && (k + 1) % kChunk == 0) {
+      stage(k + 1);
+      __syncthreads();
+    }
+  };
+  auto next_segment = [&]() __attribute__((always_inline)) {
+    finish(cur);
+    ++cur;
+    reset(st);
+    seg_bad = false;
+    if (cur < L.n) load_q(cur);
+  };
+
+  // Consume the oldest unit, refill its slot kDepth units ahead. Past the end of the run a
+  // slot re-reads its last tile (a cache hit), so the loads stay unconditional.
+  while (rec[0].live) {
+    static_for<0, kDepth>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if (rec[d].live) {
+        while (cur < rec[d].k) next_segment();
+        seg_bad |= !rec[d].ok;
+        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+      }
+      rec[d] = take();
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+    });
+  }
+  while (cur < L.n) next_segment();
+}
+
+// ---------------------------------------------------------------------------------------
+// Split mode: one workgroup per (partition s, KV head g, sequence b), S >= 2; wave w
+// streams pages j0 + w, j0 + w + 4, ... of the partition, then the four waves merge
+// through LDS into a partial result per (b, query head, s) for split_merge_kernel.
+template <KvType kKv, int kGroup>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(split_waves<kKv, kGroup>(), split_waves<kKv, kGroup>())))
 void split_kernel(Args a) {
   using Gm = Geo<kKv>;
-  constexpr int kDepth = split_depth<kKv, kGroup, kWide>();
+  constexpr int kDepth = split_depth<kKv, kGroup>();
   __shared__ float sm_acc[kWaves][kGroup][kHeadDim];
   __shared__ float sm_m[kWaves][kGroup];
   __shared__ float sm_l[kWaves][kGroup];
@@ -789,9 +1104,8 @@ void split_kernel(Args a) {
   const int nb = bad_len ? 0 : (seq_len + kBlockSize - 1) / kBlockSize;
   const int j0 = split * a.pages_per_split;
   const int j1 = min(j0 + a.pages_per_split, nb);
-  // A partition with no tokens is never read by the merge; with a single partition the
-  // workgroup still runs to write zeros (empty cache) or NaN (bad length).
-  if (a.num_splits > 1 && j0 >= j1) return;
+  // A partition with no tokens is never read by the merge.
+  if (j0 >= j1) return;
 
   const uint32_t lin = static_cast<uint32_t>(b) * hkv + g;
   QRegs<kKv, kGroup> qh;
@@ -887,15 +1201,9 @@ void split_kernel(Args a) {
     }
     const float val = any_bad ? nan : (den > 0.0f ? num / den : 0.0f);
     const float lse2 = any_bad ? nan : (den > 0.0f ? mm + __log2f(den) : kNegInf);
-    const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
-    if (a.num_splits == 1) {
-      a.out[qrow * kHeadDim + d] = val;
-      if (a.lse_out != nullptr && d == 0) a.lse_out[qrow] = lse2 * kLn2;
-    } else {
-      const size_t slot = qrow * a.num_splits + split;
-      a.part_o[slot * kHeadDim + d] = val;
-      if (d == 0) a.part_lse[slot] = lse2;
-    }
+    const size_t slot = (static_cast<size_t>(lin) * kGroup + h) * a.num_splits + split;
+    a.part_o[slot * kHeadDim + d] = val;
+    if (d == 0) a.part_lse[slot] = lse2;
   }
 }
 
@@ -999,15 +1307,15 @@ hipError_t launch_t(const Args& a, const Plan& plan, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
-  // One partition per (sequence, KV head) means many short workgroups: the wide build.
-  if (plan.num_splits == 1)
-    hipLaunchKernelGGL((split_kernel<kKv, kGroup, true>), dim3(plan.num_workgroups), dim3(kThreads),
-                       0, stream, a);
-  else
-    hipLaunchKernelGGL((split_kernel<kKv, kGroup, false>), dim3(plan.num_workgroups),
-                       dim3(kThreads), 0, stream, a);
+  if (plan.mode == Mode::kSegment) {
+    hipLaunchKernelGGL((seg_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((split_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,
+                     stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || plan.num_splits == 1) return err;
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(split_merge_kernel, dim3(a.batch * a.n_q_heads), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -1035,7 +1343,7 @@ size_t workspace_bytes(const Plan& plan, int batch, int n_q_heads, int n_kv_head
     return align256(rows * kHeadDim * sizeof(float)) + align256(rows * sizeof(float)) +
            align256(workers * 4 * sizeof(int32_t));
   }
-  if (plan.num_splits <= 1) return 0;
+  if (plan.mode == Mode::kSegment) return 0;
   const size_t rows = static_cast<size_t>(batch) * n_q_heads * plan.num_splits;
   return align256(rows * kHeadDim * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -1043,7 +1351,7 @@ size_t workspace_bytes(const Plan& plan, int batch, int n_q_heads, int n_kv_head
 void bind_workspace(Args& a, const Plan& plan, void* workspace) {
   a.part_o = a.part_lse = nullptr;
   a.pieces = nullptr;
-  if (workspace == nullptr) return;
+  if (workspace == nullptr || plan.mode == Mode::kSegment) return;
   const size_t group = static_cast<size_t>(a.n_q_heads / a.n_kv_heads);
   char* p = static_cast<char*>(workspace);
   if (plan.mode == Mode::kStream) {

@@ -17,13 +17,18 @@
  * The library reaches this with a single-pass online-normaliser softmax (xLLM README,
  * SoftMax operator) and cuts long caches into pieces whose partial (out, lse) are merged
  * by their log-sum-exp weights (swiftLLM feature list: PagedAttention v2 /
- * Flash-Decoding). Two plans cut the batch:
+ * Flash-Decoding). Three plans cut the batch:
+ *  - segment mode: a fixed grid of persistent workgroups, each taking whole
+ *    (sequence, KV head) segments, longest sequences first (for batches of at most 256
+ *    sequences; in index order beyond), its four wavefronts sharing the pages of each
+ *    segment; no partial results;
  *  - stream mode: the (sequence, KV head, page) units of the whole batch are dealt out in
  *    equal contiguous runs to a fixed grid of persistent workgroups, one run per
  *    wavefront, so every wave streams the same number of pages whatever the length mix;
- *  - split mode: one workgroup per (page partition, KV head, sequence), for a few very
- *    long caches.
- * Either only changes the order of rounding; out is the plain softmax result above.
+ *    segments cut between wavefronts are merged by a second kernel;
+ *  - split mode: one workgroup per (page partition, KV head, sequence) with at least two
+ *    partitions, merged by a second kernel; for a few very long caches.
+ * Each only changes the order of rounding; out is the plain softmax result above.
  *
  * Memory layout (all row-major and contiguous; all tensor pointers are DEVICE pointers
  * owned by the caller, for example torch tensors; the library never frees them):
@@ -51,7 +56,7 @@
  * Supported sizes: head_dim 128, block_size 16, G = n_q_heads / n_kv_heads in
  * {1, 2, 4, 8}, batch * max_blocks_per_seq * n_kv_heads < 2^31 and
  * num_pages * n_kv_heads < 2^32; stream mode also needs batch <= 4096 (the library's own
- * plan switches to split mode beyond that). Other values return
+ * plan never picks it beyond that). Other values return
  * DECODE_ATTN_ERR_UNSUPPORTED.
  *
  * Calls are asynchronous: they validate arguments on the host, enqueue kernels on
@@ -94,15 +99,17 @@ typedef enum {
 /* How a call cuts the batch into work (see the top of this file). */
 typedef enum {
   DECODE_ATTN_MODE_STREAM = 0,
-  DECODE_ATTN_MODE_SPLIT = 1
+  DECODE_ATTN_MODE_SPLIT = 1,
+  DECODE_ATTN_MODE_SEGMENT = 2
 } decode_attn_mode;
 
 /* A plan as decode_attn_plan reports it. */
 typedef struct {
   int mode;               /* decode_attn_mode */
   int num_workgroups;     /* grid of the main kernel (256 threads per workgroup) */
-  int num_splits;         /* split mode: partitions per (sequence, KV head); 0 in stream mode */
-  int pages_per_split;    /* split mode: pages per partition; 0 in stream mode */
+  int num_splits;         /* partitions per (sequence, KV head): >= 2 in split mode, 1 in
+                             segment mode, 0 in stream mode */
+  int pages_per_split;    /* split mode: pages per partition; 0 otherwise */
   size_t workspace_bytes; /* device workspace decode_attn_ex needs for this plan */
 } decode_attn_plan_t;
 
@@ -127,29 +134,36 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages,
                 int kv_dtype, float scale, float* out, hipStream_t stream);
 
 /*
- * Planning (swiftLLM feature list: Flash-Decoding). requested_splits > 0 asks for split
- * mode with that many page partitions per (sequence, KV head) (the result may be smaller:
- * it is ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits)));
- * requested_workgroups > 0 asks for stream mode on that many workgroups; at most one of
- * the two may be non-zero. With both 0 the library chooses from the shapes and num_cus
- * (the device's compute-unit count; pass 0 to query the current device, the only case
- * that calls HIP): split mode when there are fewer (sequence, KV head) pairs than compute
- * units or more than 4096 sequences, stream mode otherwise. Fills *plan and returns a
- * decode_attn_status; pure host code apart from the device query.
+ * Planning (swiftLLM feature list: Flash-Decoding). The requests:
+ *  - requested_splits == 1: segment mode, on requested_workgroups workgroups if that is
+ *    > 0, else on as many as stay resident on num_cus compute units (never more than
+ *    batch * n_kv_heads);
+ *  - requested_splits > 1 (requested_workgroups must be 0): split mode with that many page
+ *    partitions per (sequence, KV head); the result may be smaller, namely
+ *    ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits)), and a result
+ *    of 1 is segment mode;
+ *  - requested_workgroups > 0 alone: stream mode on that many workgroups;
+ *  - both 0: the library's choice from the shapes and num_cus: split mode when there are
+ *    fewer (sequence, KV head) pairs than compute units; segment mode when caches are at
+ *    most 64 pages, when there are at least two pairs per segment-mode workgroup, or when
+ *    the batch exceeds 4096 sequences; stream mode otherwise.
+ * num_cus is the device's compute-unit count; 0 queries the current device (the only HIP
+ * call, made only when the plan needs the count). kv_dtype is a decode_attn_kv_dtype (the
+ * grid of segment mode depends on it). Fills *plan and returns a decode_attn_status.
  */
 int decode_attn_plan(int batch, int max_blocks_per_seq, int n_q_heads, int n_kv_heads,
-                     int block_size, int requested_workgroups, int requested_splits, int num_cus,
-                     decode_attn_plan_t* plan);
+                     int block_size, int kv_dtype, int requested_workgroups,
+                     int requested_splits, int num_cus, decode_attn_plan_t* plan);
 
 /*
  * decode_attn with an explicit plan request and caller-owned workspace; never allocates.
  *
  * requested_workgroups and requested_splits as in decode_attn_plan (both 0 = the
  * library's choice for the current device). workspace: device memory of at least the
- * plan's workspace_bytes, 256-byte aligned; it may be NULL when that is 0. Its contents
- * on entry do not matter and on return are unspecified; it must not be in use by another
- * call still running. lse_out (nullable, 4-byte aligned) receives lse[b, h] as defined
- * above. Returns a decode_attn_status.
+ * plan's workspace_bytes, 256-byte aligned; it may be NULL when that is 0 (segment mode
+ * needs none). Its contents on entry do not matter and on return are unspecified; it must
+ * not be in use by another call still running. lse_out (nullable, 4-byte aligned)
+ * receives lse[b, h] as defined above. Returns a decode_attn_status.
  */
 int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
                    const float* k_scale, const float* v_scale,

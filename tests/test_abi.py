@@ -51,7 +51,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 3
+    assert lib.decode_attn_version() >> 16 == 4
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -108,9 +108,9 @@ def test_host_validation(lib, over, status):
     assert call(lib, **over) == status
 
 
-def plan(lib, binding, batch, mb, hq, hkv, wgs=0, splits=0, cus=256):
+def plan(lib, binding, batch, mb, hq, hkv, wgs=0, splits=0, cus=256, kv=0):
     p = binding.Plan()
-    st = lib.decode_attn_plan(batch, mb, hq, hkv, 16, wgs, splits, cus, ctypes.byref(p))
+    st = lib.decode_attn_plan(batch, mb, hq, hkv, 16, kv, wgs, splits, cus, ctypes.byref(p))
     assert st == 0, st
     return p
 
@@ -127,7 +127,7 @@ def test_explicit_plans_need_no_device_and_check_the_workspace(lib, binding):
     assert call_ex(lib, 4, 0, 9 * A, need - 1) == 3
     assert call_ex(lib, 4, 0, 9 * A + 16, need) == 3   # not 256-byte aligned
     assert call_ex(lib, -1, 0, None, 0) == 1
-    assert call_ex(lib, 4, 3, None, 0) == 1            # both requests at once
+    assert call_ex(lib, 4, 3, None, 0) == 1            # a grid with several partitions
     assert call_ex(lib, 4, 0, 9 * A, need, hq=6, hkv=4) == 1
     # Split mode with 3 partitions of 3 pages: partial rows B x Hq x S.
     s = plan(lib, binding, 2, 8, 8, 2, splits=3)
@@ -135,25 +135,35 @@ def test_explicit_plans_need_no_device_and_check_the_workspace(lib, binding):
         binding.MODE_SPLIT, 3, 3, 3 * 2 * 2)
     assert s.workspace_bytes == 2 * 8 * 3 * 128 * 4 + 256
     assert call_ex(lib, 0, 3, 9 * A, s.workspace_bytes - 1) == 3
+    # Segment mode on an explicit grid: no workspace, any grid size.
+    g = plan(lib, binding, 2, 8, 8, 2, wgs=7, splits=1)
+    assert (g.mode, g.num_workgroups, g.num_splits, g.pages_per_split, g.workspace_bytes) == (
+        binding.MODE_SEGMENT, 7, 1, 0, 0)
 
 
 def test_stream_mode_refuses_batches_beyond_the_lds_scan(lib, binding):
     p = binding.Plan()
-    assert lib.decode_attn_plan(4097, 4, 8, 8, 16, 8, 0, 0, ctypes.byref(p)) == 2
+    assert lib.decode_attn_plan(4097, 4, 8, 8, 16, 0, 8, 0, 0, ctypes.byref(p)) == 2
     auto = plan(lib, binding, 4097, 4, 8, 8)
-    assert auto.mode == binding.MODE_SPLIT
+    assert auto.mode == binding.MODE_SEGMENT
+    assert plan(lib, binding, 4097, 100, 8, 8, kv=1).mode == binding.MODE_SEGMENT
 
 
 def test_split_requests_round_to_whole_partitions(lib, binding):
     got = lambda req: (plan(lib, binding, 1, 16, 8, 8, splits=req).num_splits,
                        plan(lib, binding, 1, 16, 8, 8, splits=req).pages_per_split)
-    assert got(1) == (1, 16)
+    assert got(1) == (1, 0)       # one partition is segment mode
+    assert plan(lib, binding, 1, 16, 8, 8, splits=1).mode == binding.MODE_SEGMENT
+    assert plan(lib, binding, 1, 1, 8, 8, splits=4).mode == binding.MODE_SEGMENT
     assert got(3) == (3, 6)
     assert got(7) == (6, 3)       # ceil(16 / ceil(16 / 7))
     assert got(100) == (16, 1)
     for mb in (1, 2, 15, 36, 256, 8192):
         for req in (1, 2, 3, 5, 64):
             p = plan(lib, binding, 3, mb, 8, 4, splits=req)
+            if p.mode == binding.MODE_SEGMENT:
+                assert p.num_splits == 1 and (req == 1 or mb == 1)
+                continue
             assert p.num_splits * p.pages_per_split >= mb
             assert (p.num_splits - 1) * p.pages_per_split < mb
 
@@ -164,24 +174,50 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     p2 = plan(lib, binding, 48, 36, 32, 32)
     p3 = plan(lib, binding, 160, 256, 32, 8)
     p4 = plan(lib, binding, 1, 8192, 32, 8)
-    p5 = plan(lib, binding, 200, 34, 32, 32)
-    # Many (sequence, head) pairs over short caches: one workgroup per pair.
-    for p, b, hkv in ((p2, 48, 32), (p5, 200, 32)):
-        assert (p.mode, p.num_splits, p.num_workgroups) == (binding.MODE_SPLIT, 1, b * hkv)
+    p5 = plan(lib, binding, 200, 34, 32, 32, kv=1)
+    # Many (sequence, head) pairs over short caches: segment mode, as many workgroups as
+    # stay resident (three per compute unit), no workspace.
+    for p in (p2, p5):
+        assert (p.mode, p.num_splits, p.num_workgroups) == (binding.MODE_SEGMENT, 1, 768)
         assert p.workspace_bytes == 0
-    # Many pairs over long caches of mixed length: the balanced stream.
-    assert p3.mode == binding.MODE_STREAM and p3.num_workgroups == 512
+    # Never more workgroups than segments; the INT8 build for G = 8 spills, so it stays in
+    # stream mode.
+    assert plan(lib, binding, 3, 8, 1, 1, cus=2).num_workgroups == 3
+    assert plan(lib, binding, 3, 8, 8, 8, cus=2).num_workgroups == 6
+    assert plan(lib, binding, 300, 8, 8, 1, cus=2).mode == binding.MODE_SEGMENT
+    assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=1).mode == binding.MODE_STREAM
+    assert plan(lib, binding, 300, 8, 8, 4, cus=2).mode == binding.MODE_SEGMENT
+    # Many pairs over long caches: segment mode while every workgroup gets two segments or
+    # more (1280 pairs, 512 workgroups for G = 4), else the balanced stream.
+    assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 512
+    s3 = plan(lib, binding, 100, 256, 32, 8)
+    assert s3.mode == binding.MODE_STREAM and s3.num_workgroups == 512
     # Few long caches: split mode, about one workgroup per CU.
     assert (p4.mode, p4.num_splits, p4.pages_per_split, p4.num_workgroups) == (
         binding.MODE_SPLIT, 32, 256, 256)
     assert p1.mode == binding.MODE_SPLIT and p1.num_splits == 16
+    assert plan(lib, binding, 1, 1, 8, 8).mode == binding.MODE_SEGMENT
     assert plan(lib, binding, 160, 256, 32, 8, cus=80).num_workgroups == 160
 
 
 def test_plan_rejects_bad_arguments(lib, binding):
     p = binding.Plan()
-    assert lib.decode_attn_plan(1, 0, 8, 8, 16, 0, 0, 256, ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 8, 16, -2, 0, 256, ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 2, 2, 256, ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 6, 4, 16, 0, 0, 256, ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 0, 256, None) == 1
+    assert lib.decode_attn_plan(1, 0, 8, 8, 16, 0, 0, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, -2, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 2, 2, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 6, 4, 16, 0, 0, 0, 256, ctypes.byref(p)) == 1
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 2, 0, 0, 256, ctypes.byref(p)) == 1   # kv type
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 0, 0, 256, None) == 1
+
+
+def test_binding_plan_helper_matches_the_c_call(lib, binding):
+    # The Python helper forwards every argument in the C order.
+    p = binding.plan(200, 34, 32, 32, 16, kv_dtype="int8", num_workgroups=0, num_splits=0,
+                     num_cus=256)
+    q = plan(lib, binding, 200, 34, 32, 32, kv=1)
+    assert (p.mode, p.num_workgroups, p.num_splits, p.workspace_bytes) == (
+        q.mode, q.num_workgroups, q.num_splits, q.workspace_bytes)
+    s = binding.plan(3, 8, 8, 2, num_workgroups=5, num_splits=1, num_cus=256)
+    assert (s.mode, s.num_workgroups) == (binding.MODE_SEGMENT, 5)
+    t = binding.plan(3, 8, 8, 2, num_workgroups=5, num_cus=256)
+    assert (t.mode, t.num_workgroups) == (binding.MODE_STREAM, 5)

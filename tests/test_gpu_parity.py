@@ -74,12 +74,14 @@ SMALL = Config(0, "small_gqa", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128,
 
 # ------------------------------------------------------------------ small, every kernel variant
 
-# Plans exercised: the library's own, stream mode on several grids (64 workgroups give
+# Plans exercised: the library's own; stream mode on several grids (64 workgroups give
 # 256 workers for ~100 units, so most are empty and some sit between the pieces of a cut
-# (sequence, head) pair), and split mode with one and several partitions.
+# (sequence, head) pair); segment mode on its own grid and on one and two workgroups (every
+# workgroup then runs several segments back to back); split mode with three partitions.
 PLANS = [dict(), dict(num_workgroups=1), dict(num_workgroups=3), dict(num_workgroups=64),
-         dict(num_splits=1), dict(num_splits=3)]
-PLAN_IDS = ["auto", "wg1", "wg3", "wg64", "split1", "split3"]
+         dict(num_splits=1), dict(num_splits=1, num_workgroups=1),
+         dict(num_splits=1, num_workgroups=2), dict(num_splits=3)]
+PLAN_IDS = ["auto", "wg1", "wg3", "wg64", "seg", "seg-wg1", "seg-wg2", "split3"]
 
 
 @pytest.mark.parametrize("kv", ["fp16", "int8"])
@@ -96,7 +98,8 @@ def test_small_all_variants(torch, lib, kv, group, plan):
 
 
 @pytest.mark.parametrize("plan", [dict(num_workgroups=n) for n in (1, 2, 3, 7, 19, 64, 300)]
-                         + [dict(num_splits=n) for n in (1, 2, 3, 7, 19, 75)],
+                         + [dict(num_splits=n) for n in (1, 2, 3, 7, 19, 75)]
+                         + [dict(num_splits=1, num_workgroups=n) for n in (1, 2, 5, 6, 7)],
                          ids=lambda p: "-".join(f"{k}{v}" for k, v in p.items()))
 def test_plans_and_determinism(torch, lib, plan):
     w = generate(SMALL.with_(len_hi=1200), seed=7)
@@ -110,7 +113,8 @@ def test_plans_and_determinism(torch, lib, plan):
 
 
 EDGE_PLANS = [dict(num_workgroups=1), dict(num_workgroups=4), dict(num_workgroups=19),
-              dict(num_workgroups=100), dict(num_splits=1), dict(num_splits=4), dict(num_splits=19)]
+              dict(num_workgroups=100), dict(num_splits=1), dict(num_splits=1, num_workgroups=1),
+              dict(num_splits=1, num_workgroups=5), dict(num_splits=4), dict(num_splits=19)]
 
 
 @pytest.mark.parametrize("kv", ["fp16", "int8"])
@@ -131,7 +135,60 @@ def test_edge_lengths_and_nan_canaries(torch, lib, kv):
         assert np.all(got[lens == 0] == 0)
 
 
-@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2)], ids=["wg2", "split2"])
+@pytest.mark.parametrize("batch", [255, 256, 257])
+@pytest.mark.parametrize("grid", [0, 3, 1000])
+def test_segment_mode_order_and_grids(torch, lib, batch, grid):
+    # Segment mode ranks batches of up to 256 sequences by decreasing length inside every
+    # workgroup (ties by index) and takes larger batches in index order; segments are dealt
+    # out in a snake over the grid. Lengths from a small set make ties common; empty caches
+    # rank last. Grids: the library's, 3 workgroups (about 170 segments each, so query rows
+    # are restaged in LDS many times), and more workgroups than segments.
+    lens = np.random.default_rng(batch).choice([0, 1, 16, 17, 40, 64], size=batch)
+    cfg = SMALL.with_(batch=batch, len_lo=0, len_hi=64)
+    w = generate(cfg, seed=30, seq_lens=lens.astype(np.int32), poison=True)
+    print(f"case segment order batch={batch} grid={grid}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w, num_splits=1, num_workgroups=grid)
+    assert_parity(got, ref, f"batch {batch} grid {grid}")
+    assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_segment_mode_long_caches(torch, lib, kv):
+    # Eight (sequence, KV head) segments of up to 9000 tokens (563 pages) on one, two or
+    # eight workgroups: long runs of pages per wave across several segments, including a
+    # single-token one.
+    cfg = SMALL.with_(kv_dtype=kv, batch=4, n_q_heads=4, n_kv_heads=2, len_lo=1, len_hi=9000)
+    lens = np.array([9000, 1, 4097, 8191], dtype=np.int32)
+    w = generate(cfg, seed=50, seq_lens=lens, poison=True)
+    print(f"case long caches kv={kv}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    for grid in (1, 2, 8):
+        got, lse = gpu_run(torch, lib, w, num_splits=1, num_workgroups=grid)
+        assert_parity(got, ref, f"{kv} grid {grid}")
+        assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_segment_mode_restages_query_rows(torch, lib, kv, group):
+    # One or two workgroups over 90 (sequence, KV head) segments: more than one LDS chunk of
+    # query rows (64 / G segments) per workgroup, with lengths that leave some waves without
+    # a page in many segments.
+    cfg = SMALL.with_(kv_dtype=kv, batch=45, n_q_heads=2 * group, n_kv_heads=2, len_lo=1,
+                      len_hi=90)
+    w = generate(cfg, seed=40 + group)
+    print(f"case restage kv={kv} G={group}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    for grid in (1, 2):
+        got, lse = gpu_run(torch, lib, w, num_splits=1, num_workgroups=grid)
+        assert_parity(got, ref, f"{kv} G={group} grid {grid}")
+        assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2),
+                                  dict(num_splits=1, num_workgroups=2)],
+                         ids=["wg2", "split2", "seg2"])
 def test_all_sequences_empty(torch, lib, plan):
     cfg = SMALL.with_(len_lo=0, len_hi=40)
     w = generate(cfg, seed=3, seq_lens=np.zeros(cfg.batch, dtype=np.int32))
@@ -157,7 +214,8 @@ def test_bad_lengths_and_page_ids_give_nan_not_faults(torch, lib):
     table[5, 0] = -7
     w.seq_lens, w.block_table = lens, table
     for plan in (dict(num_workgroups=1), dict(num_workgroups=5), dict(num_workgroups=40),
-                 dict(num_splits=1), dict(num_splits=4)):
+                 dict(num_splits=1), dict(num_splits=1, num_workgroups=1),
+                 dict(num_splits=1, num_workgroups=4), dict(num_splits=4)):
         got, lse = gpu_run(torch, lib, w, **plan)
         for b in (1, 3, 4, 5):
             assert np.isnan(got[b]).all() and np.isnan(lse[b]).all(), (plan, b)
@@ -165,7 +223,9 @@ def test_bad_lengths_and_page_ids_give_nan_not_faults(torch, lib):
             assert_parity(got[b], ref[b], f"clean sequence {b} {plan}")
 
 
-@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2)], ids=["wg2", "split2"])
+@pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2),
+                                  dict(num_splits=1, num_workgroups=2)],
+                         ids=["wg2", "split2", "seg2"])
 def test_page_permutation_is_bitwise_invariant(torch, lib, plan):
     w = generate(SMALL, seed=12, extra_pages=3)
     a, _ = gpu_run(torch, lib, w, **plan)
