@@ -825,7 +825,7 @@ void seg_kernel(Args a) {
   constexpr int kDepth = seg_depth<kKv, kGroup>();
   constexpr uint32_t kQRow16 = kGroup * kHeadDim * 2 / 16;   // 16-byte words per segment's queries
   constexpr uint32_t kChunk = kSegQBytes / (kQRow16 * 16);  // segments per staged chunk
-  __shared__ uint32_t s_len[kMaxBatch];
+  __shared__ uint32_t s_len[kOrderMax];
   __shared__ int4 s_key[kOrderMax / 4];
   __shared__ uint32_t s_order[kOrderMax];
   __shared__ u32x4 s_q[kSegQBytes / 16];
@@ -841,6 +841,7 @@ void seg_kernel(Args a) {
   const int col = lane % Gm::kLanesPerRow;
   const int batch = a.batch;
   const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
+  const uint32_t mb = static_cast<uint32_t>(a.max_blocks);
 
   SegList L;
   L.w = blockIdx.x;
@@ -848,7 +849,7 @@ void seg_kernel(Args a) {
   L.hkv = hkv;
   L.max_tokens = a.max_blocks * kBlockSize;
   L.ordered = batch <= kOrderMax;
-  L.lens_in_lds = batch <= kMaxBatch;
+  L.lens_in_lds = L.ordered;   // else lengths come through scalar loads
   L.order = s_order;
   L.lens = s_len;
   L.seq_lens = a.seq_lens;
@@ -860,14 +861,14 @@ void seg_kernel(Args a) {
     L.n = full + (last < rem ? 1u : 0u);
   }
 
-  // 1. Lengths into LDS; rank the sequences by decreasing length (empty and invalid
-  //    lengths count as 0, so they come last).
-  if (L.lens_in_lds)
-    for (int b = tid; b < batch; b += kThreads) s_len[b] = static_cast<uint32_t>(a.seq_lens[b]);
+  // 1. When ordering, lengths into LDS and the rank of each sequence by decreasing length
+  //    (empty and invalid lengths count as 0, so they come last). In index order nothing
+  //    has to be read before the first loads below: lengths come through scalar loads.
   if (L.ordered) {
     int key = -1;   // pads past the batch: below every real key
     if (tid < batch) {
       const int len = a.seq_lens[tid];
+      s_len[tid] = static_cast<uint32_t>(len);
       key = len > 0 && len <= L.max_tokens ? len : 0;
     }
     reinterpret_cast<int*>(s_key)[tid] = key;
@@ -882,8 +883,8 @@ void seg_kernel(Args a) {
       }
       s_order[rank] = static_cast<uint32_t>(tid);
     }
+    __syncthreads();
   }
-  __syncthreads();
   if (L.n == 0) return;   // more workgroups than segments (same for the whole workgroup)
 
   // 2. Query rows of segments [k0, k0 + kChunk) go to LDS: each thread loads at most
@@ -950,8 +951,18 @@ void seg_kernel(Args a) {
       }
     }
   };
-  seek();
-  int32_t phys_next = ck < L.n ? scalar_load(a.block_table, static_cast<size_t>(cb) * a.max_blocks + cj) : 0;
+  // The first segment's length and this wave's first page id in it are loaded together
+  // (the page id speculatively: table entries below max_blocks are always in bounds).
+  int32_t phys_next = 0;
+  {
+    uint32_t b0, g0;
+    L.head_of<true>(0, b0, g0);
+    const int32_t first_page =
+        static_cast<uint32_t>(wave) < mb ? scalar_load(a.block_table, static_cast<size_t>(b0) * mb + wave) : 0;
+    seek();
+    if (ck < L.n)
+      phys_next = ck == 0 ? first_page : scalar_load(a.block_table, static_cast<size_t>(cb) * mb + cj);
+  }
   uint32_t last_tile = 0;
   auto take = [&]() __attribute__((always_inline)) -> SegRec {
     SegRec r;

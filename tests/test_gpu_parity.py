@@ -137,16 +137,20 @@ def test_edge_lengths_and_nan_canaries(torch, lib, kv):
 
 @pytest.mark.parametrize("batch", [255, 256, 257])
 @pytest.mark.parametrize("grid", [0, 3, 1000])
-def test_segment_mode_order_and_grids(torch, lib, batch, grid):
+@pytest.mark.parametrize("caches", ["short", "long"])
+def test_segment_mode_order_and_grids(torch, lib, batch, grid, caches):
     # Segment mode ranks batches of up to 256 sequences by decreasing length inside every
-    # workgroup (ties by index) and takes larger batches in index order; segments are dealt
-    # out in a snake over the grid. Lengths from a small set make ties common; empty caches
-    # rank last. Grids: the library's, 3 workgroups (about 170 segments each, so query rows
-    # are restaged in LDS many times), and more workgroups than segments.
-    lens = np.random.default_rng(batch).choice([0, 1, 16, 17, 40, 64], size=batch)
-    cfg = SMALL.with_(batch=batch, len_lo=0, len_hi=64)
+    # workgroup (ties by index) and takes larger batches in index order (lengths then come
+    # through scalar loads); segments are dealt out in a snake over the grid. Short and
+    # long (over 64 pages) caches.
+    # Lengths from a small set make ties common; empty caches rank last. Grids: the
+    # library's, 3 workgroups (about 170 segments each, so query rows are restaged in LDS
+    # many times), and more workgroups than segments.
+    choices = [0, 1, 16, 17, 40, 64] + ([1100, 1025] if caches == "long" else [])
+    lens = np.random.default_rng(batch).choice(choices, size=batch)
+    cfg = SMALL.with_(batch=batch, len_lo=0, len_hi=max(choices))
     w = generate(cfg, seed=30, seq_lens=lens.astype(np.int32), poison=True)
-    print(f"case segment order batch={batch} grid={grid}", flush=True)
+    print(f"case segment order batch={batch} grid={grid} caches={caches}", flush=True)
     ref, ref_lse = oracle_run(w)
     got, lse = gpu_run(torch, lib, w, num_splits=1, num_workgroups=grid)
     assert_parity(got, ref, f"batch {batch} grid {grid}")
