@@ -29,8 +29,10 @@ constexpr int kSplitWorkgroupsPerCu = 1;
 // Segment mode (no merge) is the library's choice when caches are at most this many pages
 // (whole segments are then short enough to balance without cutting them) ...
 constexpr int kShortCachePages = 64;
-// ... or when every workgroup gets at least this many segments, longest first.
+// ... or when every workgroup gets at least this many segments, longest first ...
 constexpr long long kMinSegmentsPerWorkgroup = 2;
+// ... or when there are few segments but none longer than this many pages.
+constexpr int kTinyCachePages = 16;
 
 std::mutex g_mutex;
 int g_cus[kMaxDevices];            // compute units per device, 0 = not queried yet
@@ -73,7 +75,7 @@ dattn::Plan segment_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvTyp
   if (workgroups > 0) {
     p.num_workgroups = workgroups;
   } else {
-    long long wgs = static_cast<long long>(dattn::seg_waves(kv, group)) * cus;
+    long long wgs = static_cast<long long>(dattn::seg_workgroups_per_cu(kv, group)) * cus;
     if (wgs > segments) wgs = segments;
     p.num_workgroups = wgs < 1 ? 1 : static_cast<int>(wgs);
   }
@@ -105,9 +107,13 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType k
   const bool seg_ok = !seg_spills || batch > dattn::kMaxBatch;
   // Segment mode needs a few segments per workgroup to balance whole segments, unless the
   // caches are short.
-  const long long seg_wgs = static_cast<long long>(dattn::seg_waves(kv, group)) * cus;
+  const long long seg_wgs = static_cast<long long>(dattn::seg_workgroups_per_cu(kv, group)) * cus;
   const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * seg_wgs;
   if (segments >= cus && seg_ok && (seg_balances || batch > dattn::kMaxBatch))
+    return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
+  // Few segments over caches of at most kTinyCachePages: each workgroup's run is a few
+  // round trips long, so partitions would only add the merge kernel.
+  if (segments < cus && max_blocks <= kTinyCachePages && seg_ok)
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   if (segments < cus) {
     const long long want = static_cast<long long>(kSplitWorkgroupsPerCu) * cus;

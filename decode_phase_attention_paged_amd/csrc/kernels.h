@@ -37,6 +37,12 @@ constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
 constexpr int seg_waves(KvType kv, int group) {
   return kv == KvType::kF16 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];
 }
+// Wavefronts of a segment-mode workgroup, which interleave the pages of its segment.
+constexpr int kSegW = 4;
+constexpr int kSegThreads = 64 * kSegW;
+constexpr int seg_workgroups_per_cu(KvType kv, int group) {
+  return 4 * seg_waves(kv, group) / kSegW > 0 ? 4 * seg_waves(kv, group) / kSegW : 1;
+}
 
 struct Args {
   const void* q;               // fp16 [B, Hq, D]

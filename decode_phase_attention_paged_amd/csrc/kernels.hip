@@ -818,7 +818,7 @@ struct SegRec {
 };
 
 template <KvType kKv, int kGroup>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kSegThreads)
 __attribute__((amdgpu_waves_per_eu(seg_waves(kKv, kGroup), seg_waves(kKv, kGroup))))
 void seg_kernel(Args a) {
   using Gm = Geo<kKv>;
@@ -829,10 +829,10 @@ void seg_kernel(Args a) {
   __shared__ int4 s_key[kOrderMax / 4];
   __shared__ uint32_t s_order[kOrderMax];
   __shared__ u32x4 s_q[kSegQBytes / 16];
-  __shared__ float sm_acc[2][kWaves][kGroup][kHeadDim];
-  __shared__ float sm_m[2][kWaves][kGroup];
-  __shared__ float sm_l[2][kWaves][kGroup];
-  __shared__ int sm_bad[2][kWaves];
+  __shared__ float sm_acc[2][kSegW][kGroup][kHeadDim];
+  __shared__ float sm_m[2][kSegW][kGroup];
+  __shared__ float sm_l[2][kSegW][kGroup];
+  __shared__ int sm_bad[2][kSegW];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -871,7 +871,7 @@ void seg_kernel(Args a) {
       s_len[tid] = static_cast<uint32_t>(len);
       key = len > 0 && len <= L.max_tokens ? len : 0;
     }
-    reinterpret_cast<int*>(s_key)[tid] = key;
+    if (tid < kOrderMax) reinterpret_cast<int*>(s_key)[tid] = key;
     __syncthreads();
     if (tid < batch) {
       int rank = 0;
@@ -889,14 +889,14 @@ void seg_kernel(Args a) {
 
   // 2. Query rows of segments [k0, k0 + kChunk) go to LDS: each thread loads at most
   //    kQPerThread 16-byte words of them into registers, then stores them.
-  constexpr int kQPerThread = kSegQBytes / 16 / kThreads;
+  constexpr int kQPerThread = (kSegQBytes / 16 + kSegThreads - 1) / kSegThreads;
   const u32x4* q16 = static_cast<const u32x4*>(a.q);
   u32x4 qbuf[kQPerThread];
   auto stage_load = [&](uint32_t k0) __attribute__((always_inline)) {
     const uint32_t words = min(kChunk, L.n - k0) * kQRow16;
 #pragma unroll
     for (int i = 0; i < kQPerThread; ++i) {
-      const uint32_t idx = static_cast<uint32_t>(tid + i * kThreads);
+      const uint32_t idx = static_cast<uint32_t>(tid + i * kSegThreads);
       if (idx < words) {
         const uint32_t t = idx / kQRow16;
         uint32_t b, g;
@@ -909,7 +909,7 @@ void seg_kernel(Args a) {
     const uint32_t words = min(kChunk, L.n - k0) * kQRow16;
 #pragma unroll
     for (int i = 0; i < kQPerThread; ++i) {
-      const uint32_t idx = static_cast<uint32_t>(tid + i * kThreads);
+      const uint32_t idx = static_cast<uint32_t>(tid + i * kSegThreads);
       if (idx < words) s_q[idx] = qbuf[i];
     }
   };
@@ -980,7 +980,7 @@ void seg_kernel(Args a) {
     r.k = ck;
     r.valid = cj + 1 == cnb ? clen - static_cast<int>(cnb - 1) * kBlockSize : kBlockSize;
     last_tile = r.tile;
-    cj += kWaves;
+    cj += kSegW;
     if (cj >= cnb) {
       ++ck;
       seek();
@@ -1030,19 +1030,19 @@ void seg_kernel(Args a) {
     const SegInfo s = L.info(k);
     bool any_bad = s.bad;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[slot][w] != 0;
+    for (int w = 0; w < kSegW; ++w) any_bad |= sm_bad[slot][w] != 0;
     const uint32_t lin = s.b * hkv + s.g;
     const float nan = __builtin_nanf("");
-    for (int o = tid; o < kGroup * kHeadDim; o += kThreads) {
+    for (int o = tid; o < kGroup * kHeadDim; o += kSegThreads) {
       const int h = o / kHeadDim;
       const int d = o % kHeadDim;
       float mm = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[slot][w][h]);
+      for (int w = 0; w < kSegW; ++w) mm = fmaxf(mm, sm_m[slot][w][h]);
       const float base = mm == kNegInf ? 0.0f : mm;
       float num = 0.0f, den = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < kSegW; ++w) {
         const float e = fast_exp2(sm_m[slot][w][h] - base);
         num += e * sm_acc[slot][w][h][d];
         den += e * sm_l[slot][w][h];
@@ -1319,8 +1319,8 @@ hipError_t launch_t(const Args& a, const Plan& plan, hipStream_t stream) {
     return hipGetLastError();
   }
   if (plan.mode == Mode::kSegment) {
-    hipLaunchKernelGGL((seg_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((seg_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kSegThreads),
+                       0, stream, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((split_kernel<kKv, kGroup>), dim3(plan.num_workgroups), dim3(kThreads), 0,

@@ -143,10 +143,11 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages,
  *    ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits)), and a result
  *    of 1 is segment mode;
  *  - requested_workgroups > 0 alone: stream mode on that many workgroups;
- *  - both 0: the library's choice from the shapes and num_cus: split mode when there are
- *    fewer (sequence, KV head) pairs than compute units; segment mode when caches are at
- *    most 64 pages, when there are at least two pairs per segment-mode workgroup, or when
- *    the batch exceeds 4096 sequences; stream mode otherwise.
+ *  - both 0: the library's choice from the shapes and num_cus: with fewer (sequence, KV
+ *    head) pairs than compute units, segment mode for caches of at most 16 pages and split
+ *    mode otherwise; with more, segment mode when caches are at most 64 pages, when there
+ *    are at least two pairs per segment-mode workgroup, or when the batch exceeds 4096
+ *    sequences, and stream mode otherwise.
  * num_cus is the device's compute-unit count; 0 queries the current device (the only HIP
  * call, made only when the plan needs the count). kv_dtype is a decode_attn_kv_dtype (the
  * grid of segment mode depends on it). Fills *plan and returns a decode_attn_status.

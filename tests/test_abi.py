@@ -195,8 +195,12 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     # Few long caches: split mode, about one workgroup per CU.
     assert (p4.mode, p4.num_splits, p4.pages_per_split, p4.num_workgroups) == (
         binding.MODE_SPLIT, 32, 256, 256)
-    assert p1.mode == binding.MODE_SPLIT and p1.num_splits == 16
+    # Few pairs over caches of at most 16 pages: segment mode (one workgroup per pair);
+    # longer caches: split mode.
+    assert (p1.mode, p1.num_workgroups) == (binding.MODE_SEGMENT, 8)
     assert plan(lib, binding, 1, 1, 8, 8).mode == binding.MODE_SEGMENT
+    p17 = plan(lib, binding, 1, 17, 8, 8)
+    assert p17.mode == binding.MODE_SPLIT and p17.num_splits == 17
     assert plan(lib, binding, 160, 256, 32, 8, cus=80).num_workgroups == 160
 
 
