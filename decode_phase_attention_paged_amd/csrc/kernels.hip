@@ -61,7 +61,8 @@ struct Geo {
   static constexpr int kLanesPerRow = kHeadDim / kChunk;    // 16 | 8
   static constexpr int kRows = kWave / kLanesPerRow;        // lane rows: 4 | 8
   static constexpr int kLoads = kBlockSize / kRows;         // loads per tile: 4 | 2
-  static constexpr int kTileBytes = kBlockSize * kHeadDim * kElem;
+  static constexpr int kRowBytes = kHeadDim * kElem;
+  static constexpr int kTileBytes = kBlockSize * kRowBytes;
   static constexpr bool kScaled = kKv == KvType::kI8;
   static constexpr int kPairs = kChunk / 2;                 // fp16 pairs per lane per load
 
@@ -199,17 +200,33 @@ struct Tile {
 
 // Tile index = phys * Hkv + g. A unit whose page id failed the range check reads tile 0
 // instead (its output is NaN whatever is read), so every load targets a valid tile.
+// `valid` is the number of the page's tokens inside the sequence. On a partly filled last
+// page (0 < valid < 16) the lanes of rows at or past `valid` load the last valid row
+// instead: their addresses fall in cache lines the wave reads anyway, so rows the softmax
+// masks out cost no HBM traffic. Other values (full pages, and units that only re-read an
+// earlier tile) load the whole tile with immediate offsets.
 template <KvType kKv>
 __device__ __forceinline__ void load_tile(Tile<kKv>& t, const Args& a, uint32_t tile_index,
-                                          int lane) {
+                                          int lane, int valid) {
   using Gm = Geo<kKv>;
   const size_t base = static_cast<size_t>(tile_index) * Gm::kTileBytes;
   const char* kb = static_cast<const char*>(a.k_pages) + base;
   const char* vb = static_cast<const char*>(a.v_pages) + base;
+  if (valid <= 0 || valid >= kBlockSize) {
 #pragma unroll
-  for (int i = 0; i < Gm::kLoads; ++i) {
-    t.k[i] = *reinterpret_cast<const u32x4*>(kb + Gm::offset(lane, i));
-    t.v[i] = *reinterpret_cast<const u32x4*>(vb + Gm::offset(lane, i));
+    for (int i = 0; i < Gm::kLoads; ++i) {
+      t.k[i] = *reinterpret_cast<const u32x4*>(kb + Gm::offset(lane, i));
+      t.v[i] = *reinterpret_cast<const u32x4*>(vb + Gm::offset(lane, i));
+    }
+  } else {
+    const int row = lane / Gm::kLanesPerRow;
+    const int in_row = (lane % Gm::kLanesPerRow) * 16;
+#pragma unroll
+    for (int i = 0; i < Gm::kLoads; ++i) {
+      const int off = min(Gm::token(row, i), valid - 1) * Gm::kRowBytes + in_row;
+      t.k[i] = *reinterpret_cast<const u32x4*>(kb + off);
+      t.v[i] = *reinterpret_cast<const u32x4*>(vb + off);
+    }
   }
   if constexpr (Gm::kScaled) {
     const size_t srow = static_cast<size_t>(tile_index) * kBlockSize + 2 * (lane / Gm::kLanesPerRow);
@@ -537,7 +554,7 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
       constexpr int d = decltype(dc)::value;
       if constexpr (d == 0) rec[0] = take();
       else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
 
     State<kKv, kGroup> st;
@@ -590,7 +607,7 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
         const uint32_t k = k0 + d;
         process(k, rec[d], tiles[d]);
         if (k + kDepth < n) rec[d] = take();
-        load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+        load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
     static_for<0, kDepth>([&](auto dc) {
@@ -994,7 +1011,7 @@ void seg_kernel(Args a) {
   static_for<0, kDepth>([&](auto dc) {
     constexpr int d = decltype(dc)::value;
     rec[d] = take();
-    load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+    load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
   });
   stage_store(0);
   __syncthreads();
@@ -1076,7 +1093,7 @@ void seg_kernel(Args a) {
         consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
       }
       rec[d] = take();
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
   }
   while (cur < L.n) next_segment();
@@ -1154,7 +1171,7 @@ void split_kernel(Args a) {
       constexpr int d = decltype(dc)::value;
       if constexpr (d == 0) rec[0] = take();
       else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
     uint32_t k0 = 0;
     for (; k0 + kDepth <= n; k0 += kDepth) {
@@ -1163,7 +1180,7 @@ void split_kernel(Args a) {
         bad |= !rec[d].ok;
         consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
         if (k0 + d + kDepth < n) rec[d] = take();
-        load_tile<kKv>(tiles[d], a, rec[d].tile, lane);
+        load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
     static_for<0, kDepth>([&](auto dc) {
