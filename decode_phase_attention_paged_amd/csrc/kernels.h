@@ -31,7 +31,7 @@ enum class Mode { kStream = 0, kSplit = 1, kSegment = 2 };
 constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
 // Waves per SIMD the segment-mode kernel is compiled for, by storage type and log2 G; the
-// host sizes that mode's grid to this many workgroups per compute unit.
+// host sizes that mode's grid to the workgroups that stay resident at that occupancy.
 constexpr int kSegWavesF16[4] = {3, 2, 2, 1};
 constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
 constexpr int seg_waves(KvType kv, int group) {

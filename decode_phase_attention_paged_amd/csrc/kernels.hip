@@ -8,26 +8,28 @@
 // head (GQA, xLLM README optimisation list), finishes the dot products with DPP reductions
 // inside each token row of 16 lanes (fp16) or 8 lanes (int8), and folds the scores into a
 // running max / running sum softmax per lane row (the online normaliser of the xLLM README
-// SoftMax operator). Segments cut between workers leave partial (output, log-sum-exp)
-// pairs that a second kernel merges by their log-sum-exp weights in a fixed order
-// (PagedAttention v2 / Flash-Decoding, swiftLLM feature list). No atomics anywhere, so a
-// given grid gives bitwise-identical results.
+// SoftMax operator). Where a segment is cut between workers, the pieces leave partial
+// (output, log-sum-exp) pairs that a second kernel merges by their log-sum-exp weights in
+// a fixed order (PagedAttention v2 / Flash-Decoding, swiftLLM feature list). No atomics
+// anywhere, so a given plan gives bitwise-identical results.
 //
-// Two ways of cutting the batch into work:
+// Three ways of cutting the batch into work:
+//  * segment mode: a fixed grid of persistent workgroups takes whole segments, longest
+//    sequences first; a workgroup's four waves share each segment's pages and merge their
+//    states in LDS, so nothing is cut and no second kernel runs. Used for most batches.
 //  * stream mode: a fixed grid of persistent workgroups; units are numbered b-major, then
 //    g, then j, and wavefront w of W takes units [w T / W, (w + 1) T / W) of the T units.
-//    Every wave streams the same number of pages whatever the mix of lengths, so no wave
-//    waits on a long tail. Used when the batch has many segments.
+//    Every wave streams the same number of pages whatever the mix of lengths. Used when
+//    segments are too few or too long to balance whole.
 //  * split mode: one workgroup per (page partition, g, b), its four waves interleaving the
-//    partition's pages and merging in LDS. Used for a few very long caches, where stream
-//    mode would cut each segment into hundreds of pieces.
+//    partition's pages and merging in LDS. Used for a few very long caches.
 //
 // The path is bound by HBM bandwidth: per token and KV head it reads 2 * 128 * 2 bytes
 // (fp16) for 4 * G * 128 flops, far below the VALU or MFMA ridge point, so the design
 // spends its effort on keeping loads in flight, not on matrix cores. The only vector
 // memory operations inside the streaming loops are the tile loads: page ids come through
-// scalar loads and query rows from LDS, so the compiler can wait for exactly the oldest
-// tile and leave the newer ones in flight.
+// scalar loads (or LDS) and query rows from LDS, so the compiler can wait for exactly the
+// oldest tile and leave the newer ones in flight.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -90,9 +92,9 @@ constexpr int kSplitDepthI8[4] = {6, 4, 3, 2};
 constexpr int kSplitWavesF16[4] = {1, 1, 1, 1};
 constexpr int kSplitWavesI8[4] = {1, 1, 1, 1};
 // Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
+// Many resident workgroups with shallow rings measured faster than deep rings.
 constexpr int kSegDepthF16[4] = {2, 2, 2, 2};
 constexpr int kSegDepthI8[4] = {1, 3, 2, 1};
-
 
 template <KvType kKv, int kGroup>
 constexpr int stream_depth() {
