@@ -158,6 +158,36 @@ def test_segment_mode_order_and_grids(torch, lib, batch, grid, caches):
 
 
 @pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_stream_mode_query_rows_beyond_lds(torch, lib, kv):
+    # Stream mode stages a workgroup's query rows in LDS when they fit in 16 KiB; one
+    # workgroup over 80 (sequence, KV head) segments of G = 8 (2 KiB of query rows each)
+    # takes them from global memory instead, as does every workgroup of a 3-workgroup grid.
+    cfg = SMALL.with_(kv_dtype=kv, batch=40, n_q_heads=16, n_kv_heads=2, len_lo=1, len_hi=70)
+    w = generate(cfg, seed=60)
+    print(f"case stream global queries kv={kv}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    for grid in (1, 3):
+        got, lse = gpu_run(torch, lib, w, num_workgroups=grid)
+        assert_parity(got, ref, f"{kv} grid {grid}")
+        assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("longest", [40000, 70000])
+def test_split_mode_partitions_beyond_one_table_chunk(torch, lib, longest):
+    # A split workgroup stages its partition's table entries in LDS 1024 pages at a time;
+    # two partitions of 40000 or 70000 tokens (1250 or 2188 pages each) need two or three
+    # chunks; the shorter sequence ends inside its second chunk.
+    cfg = SMALL.with_(batch=2, n_q_heads=4, n_kv_heads=1, len_lo=1, len_hi=longest)
+    lens = np.array([longest, 2049 * 16 + 5], dtype=np.int32)
+    w = generate(cfg, seed=61, seq_lens=lens, poison=True)
+    print(f"case split chunks longest={longest}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w, num_splits=2)
+    assert_parity(got, ref, f"longest {longest}")
+    assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
 def test_segment_mode_long_caches(torch, lib, kv):
     # Eight (sequence, KV head) segments of up to 9000 tokens (563 pages) on one, two or
     # eight workgroups: long runs of pages per wave across several segments, including a
