@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for decode-phase paged attention.
+"""CPU oracle for decode-phase paged attention (fp64) and for appending a decode
+step's K/V rows to the paged cache.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by ``__graft_entry__.smoke()``
 and by the CPU-baseline leg of ``bench.py``, never by the library.
@@ -11,3 +12,4 @@ from .decode import (  # noqa: F401
     gather_sequence,
     kv_head_of,
 )
+from .append import append_kv, quantize_row  # noqa: F401
