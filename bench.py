@@ -39,9 +39,11 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources that decide what the attention kernels do (kernels, their
+    internal interface and the host planner)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_phase_attention_paged_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in ("api.cpp", "kernels.h", "kernels.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

@@ -55,6 +55,7 @@ _SIGNATURES = {
     "decode_attn_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                             _P, _I, _I, _P, _SZ, _P]),
     "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
+    "decode_attn_append": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
 }
@@ -222,3 +223,59 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
                                 _stream(q.device))
     _check(st, "decode_attn_ex")
     return out
+
+
+def decode_attn_append(k_new, v_new, block_table, positions, k_pages, v_pages, *,
+                       k_scale=None, v_scale=None):
+    """Write each sequence's new K/V row (fp16 [batch, n_kv_heads, head_dim]) into its
+    page slot, in place: row (b, g) goes to page block_table[b, p // bs], slot p % bs,
+    with p = positions[b] (int32; p < 0 skips b). INT8 pools (with k_scale / v_scale)
+    store per-row codes and scales (see decode_attn_append in include/decode_attn.h).
+    The work is enqueued on torch's current stream of k_new's device."""
+    lib = load_library()
+    dev = k_new.device
+    if dev.type != "cuda":
+        raise ValueError("decode_attn_append runs on the GPU only; k_new is on " + str(dev))
+    named = dict(k_new=k_new, v_new=v_new, block_table=block_table, positions=positions,
+                 k_pages=k_pages, v_pages=v_pages)
+    if k_scale is not None or v_scale is not None:
+        named.update(k_scale=k_scale, v_scale=v_scale)
+    for name, t in named.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_new.dtype != torch.float16 or k_new.dim() != 3 or v_new.shape != k_new.shape \
+            or v_new.dtype != torch.float16:
+        raise ValueError("k_new and v_new must be fp16 [batch, n_kv_heads, head_dim]")
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages must both be [num_pages, n_kv_heads, block_size, head_dim]")
+    if k_pages.dtype == torch.float16:
+        kv = KV_FP16
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("row scales are only for int8 caches")
+    elif k_pages.dtype == torch.int8:
+        kv = KV_INT8
+        if k_scale is None or v_scale is None:
+            raise ValueError("int8 caches need k_scale and v_scale")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_pages.shape[:3]):
+                raise ValueError("row scales must be fp32 [num_pages, n_kv_heads, block_size]")
+    else:
+        raise ValueError("k_pages must be fp16 or int8")
+    batch, n_kv, head_dim = k_new.shape
+    num_pages, pool_kv, block_size, pool_d = k_pages.shape
+    if (pool_kv, pool_d) != (n_kv, head_dim):
+        raise ValueError("the new rows' heads or head_dim differ from the pools'")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be int32 [batch, max_blocks_per_seq]")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (batch,):
+        raise ValueError("positions must be int32 [batch]")
+    with torch.cuda.device(dev):
+        st = lib.decode_attn_append(_ptr(k_new), _ptr(v_new), _ptr(block_table), _ptr(positions),
+                                    batch, block_table.shape[1], num_pages, n_kv, head_dim,
+                                    block_size, kv, _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                    _ptr(v_scale), _stream(dev))
+    _check(st, "decode_attn_append")

@@ -16,7 +16,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (4 << 16) | 0;
+constexpr int kVersion = (5 << 16) | 0;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -334,6 +334,51 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages, const f
   return run(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, batch,
              max_blocks_per_seq, num_pages, n_q_heads, n_kv_heads, kv_dtype, scale, out, nullptr,
              plan, ws, stream);
+}
+
+int decode_attn_append(const void* k_new, const void* v_new, const int32_t* block_table,
+                       const int32_t* positions, int batch, int max_blocks_per_seq,
+                       int num_pages, int n_kv_heads, int head_dim, int block_size,
+                       int kv_dtype, void* k_pages, void* v_pages, float* k_scale,
+                       float* v_scale, hipStream_t stream) {
+  if (batch < 0 || max_blocks_per_seq < 1 || num_pages < 1 || n_kv_heads < 1 ||
+      head_dim < 1 || block_size < 1)
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (kv_dtype != DECODE_ATTN_KV_FP16 && kv_dtype != DECODE_ATTN_KV_INT8)
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  const bool int8 = kv_dtype == DECODE_ATTN_KV_INT8;
+  if (int8 != (k_scale != nullptr) || int8 != (v_scale != nullptr))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (batch > 0 && (k_new == nullptr || v_new == nullptr || block_table == nullptr ||
+                    positions == nullptr || k_pages == nullptr || v_pages == nullptr))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) ||
+      !aligned(v_pages, 16) || !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
+      !aligned(block_table, 4) || !aligned(positions, 4))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (head_dim != kHeadDim || block_size != kBlockSize) return DECODE_ATTN_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_blocks_per_seq) * block_size > INT_MAX ||
+      static_cast<long long>(batch) * n_kv_heads > INT_MAX ||
+      static_cast<long long>(batch) * max_blocks_per_seq > INT_MAX ||
+      static_cast<long long>(num_pages) * n_kv_heads > UINT32_MAX)
+    return DECODE_ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return DECODE_ATTN_OK;
+  (void)hipGetLastError();  // start from a clean error state
+  dattn::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_table = block_table;
+  a.positions = positions;
+  a.k_pages = k_pages;
+  a.v_pages = v_pages;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.batch = batch;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_pages = num_pages;
+  a.n_kv_heads = n_kv_heads;
+  if (dattn::launch_append(kv_of(kv_dtype), a, stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
 }
 
 const char* decode_attn_status_string(int status) {

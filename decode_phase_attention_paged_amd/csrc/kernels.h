@@ -85,4 +85,21 @@ void bind_workspace(Args& a, const Plan& plan, void* workspace);
 // Enqueue the main kernel and the merge of the partial results it leaves.
 hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStream_t stream);
 
+// Appending a decode step's new K/V rows to the paged cache (append.hip).
+struct AppendArgs {
+  const void* k_new;           // fp16 [B, Hkv, D]
+  const void* v_new;
+  const int32_t* block_table;  // int32 [B, MB]
+  const int32_t* positions;    // int32 [B]: token position of the new row, < 0 = none
+  void* k_pages;               // fp16 | int8 [NP, Hkv, bs, D]
+  void* v_pages;
+  float* k_scale;              // fp32 [NP, Hkv, bs] (int8 only)
+  float* v_scale;
+  int batch;
+  int max_blocks;              // MB
+  int num_pages;               // NP
+  int n_kv_heads;
+};
+hipError_t launch_append(KvType kv, const AppendArgs& a, hipStream_t stream);
+
 }  // namespace dattn

@@ -175,6 +175,39 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
                    int requested_workgroups, int requested_splits,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Append a decode step's new key and value rows to the paged cache: every decode step
+ * adds the new token's K and V before attending (page "Eine LLM-Inferenz-Engine von
+ * Grund auf mit C++ und CUDA bauen", section 1.1), and token position p of sequence b
+ * lives in page block_table[b, p / block_size], slot p % block_size (swiftLLM feature
+ * list: PagedAttention).
+ *
+ *     k_new, v_new  fp16 [batch, n_kv_heads, head_dim], 16-byte aligned: the new rows.
+ *     positions     int32 [batch]: the new token's position p_b in sequence b (its
+ *                   length before the step); p_b < 0 means no new token for b.
+ *     block_table   as for decode_attn; entry (b, p_b / block_size) must name the page
+ *                   that receives the row (the caller allocates pages).
+ *     k_pages, v_pages (and k_scale, v_scale for INT8) as for decode_attn, written in
+ *                   place: row (b, g) goes to [page, g, p_b % block_size]. Nothing else
+ *                   in the pools is touched.
+ *
+ * FP16 pools store the row unchanged. INT8 pools (xLLM README, quantisation list:
+ * per-row INT8) store symmetric codes: s = max_d |x_d| / 127 and code_d = rint(x_d / s)
+ * (round half to even), both in fp32 with IEEE division, clamped to [-127, 127]; a row of
+ * zeros stores s = 0 and codes 0. Rows must be finite.
+ *
+ * Bad device values never fault: a row whose position is at or past
+ * max_blocks_per_seq * block_size, or whose table entry lies outside [0, num_pages), is
+ * not written. Two sequences whose positions map to the same page slot race (the caller
+ * must not do that). Asynchronous on `stream`; never allocates. Supported sizes: as for
+ * decode_attn, plus batch * n_kv_heads < 2^31. Returns a decode_attn_status.
+ */
+int decode_attn_append(const void* k_new, const void* v_new, const int32_t* block_table,
+                       const int32_t* positions, int batch, int max_blocks_per_seq,
+                       int num_pages, int n_kv_heads, int head_dim, int block_size,
+                       int kv_dtype, void* k_pages, void* v_pages, float* k_scale,
+                       float* v_scale, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);
 

@@ -34,8 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "decode_attn", "decode_attn_ex", "decode_attn_plan", "decode_attn_status_string",
-        "decode_attn_version"])
+        "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_plan",
+        "decode_attn_status_string", "decode_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,7 +51,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 4
+    assert lib.decode_attn_version() >> 16 == 5
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -225,3 +225,39 @@ def test_binding_plan_helper_matches_the_c_call(lib, binding):
     assert (s.mode, s.num_workgroups) == (binding.MODE_SEGMENT, 5)
     t = binding.plan(3, 8, 8, 2, num_workgroups=5, num_cus=256)
     assert (t.mode, t.num_workgroups) == (binding.MODE_STREAM, 5)
+
+
+# decode_attn_append: fake device addresses again; every case fails host-side validation
+# (or enqueues nothing) before the first HIP call.
+APPEND = dict(k=A, v=2 * A, bt=3 * A, pos=4 * A, batch=2, mb=8, np_=16, hkv=2, d=128, bs=16,
+              kv=0, kp=5 * A, vp=6 * A, ks=None, vs=None)
+
+
+def call_append(lib, **over):
+    a = dict(APPEND, **over)
+    return lib.decode_attn_append(a["k"], a["v"], a["bt"], a["pos"], a["batch"], a["mb"],
+                                  a["np_"], a["hkv"], a["d"], a["bs"], a["kv"], a["kp"],
+                                  a["vp"], a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(kv=1), 1),                         # int8 without row scales
+    (dict(ks=7 * A, vs=8 * A), 1),           # fp16 with row scales
+    (dict(kv=3), 1),
+    (dict(k=None), 1),
+    (dict(kp=None), 1),
+    (dict(pos=None), 1),
+    (dict(k=A + 8), 1),                      # new rows not 16-byte aligned
+    (dict(kp=5 * A + 4), 1),                 # pools not 16-byte aligned
+    (dict(kv=1, ks=7 * A + 2, vs=8 * A), 1), # scales not 4-byte aligned
+    (dict(batch=-1), 1),
+    (dict(mb=0), 1),
+    (dict(np_=0), 1),
+    (dict(hkv=0), 1),
+    (dict(d=64), 2),
+    (dict(bs=8), 2),
+    (dict(batch=1 << 20, hkv=4096), 2),      # batch * Hkv beyond 31 bits
+    (dict(batch=0, k=None, v=None, bt=None, pos=None, kp=None, vp=None), 0),
+])
+def test_append_host_validation(lib, over, status):
+    assert call_append(lib, **over) == status

@@ -1,0 +1,162 @@
+"""GPU parity of decode_attn_append against the oracle: the written pools must be
+bit-identical (fp16 rows copied, INT8 codes and fp32 scales decided in the same fp32
+arithmetic), nothing else in the pools may change, rows with no position, a position
+beyond the table or a bad page id are skipped, and attention over the grown cache matches
+the oracle's attention over its own grown cache. Every call goes through the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_phase_attention_paged_amd.workload import CONFIGS, generate
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need an MI355X"
+    return t
+
+
+@pytest.fixture(scope="module")
+def lib(torch):
+    from decode_phase_attention_paged_amd import binding
+    return binding
+
+
+def dev(torch, a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def grown_cache(cfg, seed, rng, extra_pages=3):
+    """A workload plus, for every sequence, a page for the token at position L_b, and
+    random new rows (with a zero row and a single-element row among them)."""
+    w = generate(cfg, seed=seed, extra_pages=extra_pages)
+    table = w.block_table.copy()
+    lens = w.seq_lens.copy()
+    pools = [w.k_pages, w.v_pages]
+    scales = [w.k_scale, w.v_scale]
+    need = 0
+    for b in range(cfg.batch):
+        j = int(lens[b]) // cfg.block_size
+        if j < table.shape[1] and table[b, j] < 0:
+            table[b, j] = w.num_pages + need
+            need += 1
+    if need:
+        shape = (need,) + w.k_pages.shape[1:]
+        if cfg.kv_dtype == "int8":
+            add = [rng.integers(-127, 128, size=shape).astype(np.int8) for _ in range(2)]
+            scales = [np.concatenate([s, rng.uniform(0.01, 0.02, size=shape[:3]).astype(np.float32)])
+                      for s in scales]
+        else:
+            add = [rng.standard_normal(shape).astype(np.float16) for _ in range(2)]
+        pools = [np.concatenate([p, a]) for p, a in zip(pools, add)]
+    new = [(rng.standard_normal((cfg.batch, cfg.n_kv_heads, cfg.head_dim)) *
+            rng.uniform(0.1, 10, size=(cfg.batch, cfg.n_kv_heads, 1))).astype(np.float16)
+           for _ in range(2)]
+    new[0][0, 0] = 0.0                       # a zero row
+    new[1][0, 0] = 0.0
+    new[1][0, 0, 5] = -3.0                   # a single-element row
+    return w, table, lens, pools, scales, new
+
+
+def run_append(torch, lib, table, positions, pools, scales, new):
+    d = [dev(torch, a) for a in (table, positions, pools[0], pools[1], new[0], new[1])]
+    ks, vs = dev(torch, scales[0]), dev(torch, scales[1])
+    lib.decode_attn_append(d[4], d[5], d[0], d[1], d[2], d[3], k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return host(d[2]), host(d[3]), host(ks), host(vs)
+
+
+CASES = [("small_fp16", 1, dict(batch=5, n_q_heads=6, n_kv_heads=3, len_lo=0, len_hi=70)),
+         ("small_int8", 1, dict(batch=5, n_q_heads=6, n_kv_heads=3, len_lo=0, len_hi=70,
+                                kv_dtype="int8")),
+         ("llama2_7b_mha_b48", 2, {}),
+         ("int8_mha_b200", 5, {})]
+
+
+@pytest.mark.parametrize("name,index,over", CASES, ids=[c[0] for c in CASES])
+def test_append_is_bit_exact(torch, lib, name, index, over):
+    cfg = CONFIGS[index].with_(**over)
+    rng = np.random.default_rng(70 + index)
+    w, table, lens, pools, scales, new = grown_cache(cfg, 70 + index, rng)
+    assert cfg.batch >= 5
+    positions = lens.copy()
+    positions[1] = -1                                     # no new token
+    positions[2] = 16 * (int(lens[2]) // 16)              # slot 0 of its page
+    positions[3] = cfg.max_blocks_per_seq * 16            # beyond the table: skipped
+    positions[4] = 15                                     # slot 15 of page 0 ...
+    table[4, 0] = pools[0].shape[0]                       # ... which is out of range: skipped
+    print(f"case append {name} rows={cfg.batch * cfg.n_kv_heads}", flush=True)
+    got = run_append(torch, lib, table, positions, pools, scales, new)
+    expect_pos = positions.copy()
+    expect_pos[3] = expect_pos[4] = -1                    # what the library must skip
+    want = oracle.append_kv(pools[0], pools[1], table, expect_pos, new[0], new[1],
+                            cfg.block_size, scales[0], scales[1])
+    for g, x, what in zip(got, want, ("k_pages", "v_pages", "k_scale", "v_scale")):
+        if x is None:
+            assert g is None
+            continue
+        assert g.dtype == x.dtype and g.shape == x.shape
+        bits = {1: np.uint8, 2: np.uint16, 4: np.uint32}[g.itemsize]
+        bad = np.argwhere(g.view(bits) != x.view(bits))
+        assert bad.size == 0, f"{what}: {len(bad)} elements differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_three_steps_then_attention(torch, lib, kv):
+    # Three decode steps: append at L_b, L_b + 1, L_b + 2 (crossing page boundaries for some
+    # sequences), then attend over L_b + 3 tokens; the GPU pools stay bit-identical to the
+    # oracle's, and the attention matches the oracle's within the decode tolerance.
+    cfg = CONFIGS[1].with_(batch=6, n_q_heads=8, n_kv_heads=2, len_lo=13, len_hi=60,
+                           kv_dtype=kv)
+    rng = np.random.default_rng(80)
+    w = generate(cfg, seed=80, extra_pages=0)
+    table = w.block_table.copy()
+    lens = w.seq_lens.copy()
+    pools = [w.k_pages, w.v_pages]
+    scales = [w.k_scale, w.v_scale]
+    # pages for tokens up to L_b + 2
+    extra = 0
+    for b in range(cfg.batch):
+        for p in range(int(lens[b]), int(lens[b]) + 3):
+            j = p // cfg.block_size
+            if table[b, j] < 0:
+                table[b, j] = w.num_pages + extra
+                extra += 1
+    if extra:
+        shape = (extra,) + w.k_pages.shape[1:]
+        pools = [np.concatenate([p, np.zeros(shape, dtype=p.dtype)]) for p in pools]
+        if kv == "int8":
+            scales = [np.concatenate([s, np.zeros(shape[:3], dtype=np.float32)]) for s in scales]
+    d_tab = dev(torch, table)
+    d_k, d_v = dev(torch, pools[0]), dev(torch, pools[1])
+    d_ks, d_vs = dev(torch, scales[0]), dev(torch, scales[1])
+    ref = [pools[0], pools[1], scales[0], scales[1]]
+    for step in range(3):
+        pos = (lens + step).astype(np.int32)
+        new = [rng.standard_normal((cfg.batch, cfg.n_kv_heads, 128)).astype(np.float16)
+               for _ in range(2)]
+        lib.decode_attn_append(dev(torch, new[0]), dev(torch, new[1]), d_tab, dev(torch, pos),
+                               d_k, d_v, k_scale=d_ks, v_scale=d_vs)
+        ref = list(oracle.append_kv(ref[0], ref[1], table, pos, new[0], new[1],
+                                    cfg.block_size, ref[2], ref[3]))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(d_k), ref[0]) and np.array_equal(host(d_v), ref[1])
+    if kv == "int8":
+        assert np.array_equal(host(d_ks), ref[2]) and np.array_equal(host(d_vs), ref[3])
+    grown = (lens + 3).astype(np.int32)
+    out = lib.decode_attn(dev(torch, w.q), d_k, d_v, d_tab, dev(torch, grown), w.scale,
+                          k_scale=d_ks, v_scale=d_vs)
+    torch.cuda.synchronize()
+    want, _ = oracle.decode_attention(w.q, ref[0], ref[1], table, grown, w.scale, ref[2], ref[3])
+    diff = np.abs(host(out).astype(np.float64) - want)
+    assert np.all(diff <= ATOL + RTOL * np.abs(want)), f"max|d|={diff.max():.3e}"
