@@ -8,8 +8,18 @@ The five presets stand in for the workloads the pages talk about: a
 Llama-2-7B-shaped MHA batch and a Llama-3-8B-shaped GQA batch (xLLM README,
 benchmark section; swiftLLM README, performance section), one very long
 context (the long-context case of the C++/CUDA engine blog, section 3.4), and
-a per-row INT8 cache (xLLM README, quantisation list). No weights, prompts or
-datasets are involved: values are random with the stated distributions.
+a per-row INT8 cache (xLLM README, quantisation list). Two more carry the other
+storage formats the pages name: a BF16 cache (xLLM README, quantisation list:
+"FP16, BF16") on the Llama-2-7B batch, and an FP8 E4M3 cache with per-row
+scales (C++/CUDA engine blog, section 4) on the INT8 batch's shape. No weights,
+prompts or datasets are involved: values are random with the stated
+distributions.
+
+BF16 values are drawn as fp32 N(0, 1) and kept as the upper 16 bits of each
+fp32 word (numpy has no bf16 type, so bf16 arrays hold uint16 bit patterns);
+for a BF16 cache q is bf16 too. FP8 codes are uniform over the 254 finite E4M3
+codes (every code but 0x7F and 0xFF), with row scales U(0.005, 0.02) * 127/448,
+so that the largest code reaches the magnitude of the INT8 preset's largest.
 
 Draw order for a given seed is fixed:
   seq_lens -> page permutation -> q -> K -> V -> peaky rows -> (k_scale, v_scale)
@@ -44,7 +54,7 @@ class Config:
     block_size: int
     len_lo: int                 # seq_lens ~ integer uniform on [len_lo, len_hi]
     len_hi: int
-    kv_dtype: str               # "fp16" or "int8"
+    kv_dtype: str               # "fp16", "bf16", "int8" or "fp8"
     identity_table: bool = False
     peaky_fraction: float = 0.0  # fraction of each (sequence, KV head)'s keys scaled
     peaky_factor: float = 1.0
@@ -70,17 +80,23 @@ CONFIGS = {
     4: Config(4, "long_ctx_gqa_131k", 1, 32, 8, 128, 16, 131072, 131072, "fp16",
               peaky_fraction=0.01, peaky_factor=8.0),
     5: Config(5, "int8_mha_b200", 200, 32, 32, 128, 16, 18, 530, "int8"),
+    6: Config(6, "llama2_7b_mha_b48_bf16", 48, 32, 32, 128, 16, 18, 563, "bf16"),
+    7: Config(7, "fp8_mha_b200", 200, 32, 32, 128, 16, 18, 530, "fp8"),
 }
+
+# Storage bytes per element and per row scale, by kv_dtype.
+ELEM_BYTES = {"fp16": 2, "bf16": 2, "int8": 1, "fp8": 1}
+SCALE_BYTES = {"fp16": 0, "bf16": 0, "int8": 4, "fp8": 4}
 
 
 @dataclass
 class Workload:
     config: Config
     seed: int
-    q: np.ndarray             # fp16 [B, Hq, D]
-    k_pages: np.ndarray       # fp16 | int8 [NP, Hkv, bs, D]
-    v_pages: np.ndarray
-    k_scale: Optional[np.ndarray]   # fp32 [NP, Hkv, bs] for int8, else None
+    q: np.ndarray             # fp16 [B, Hq, D]; bf16 bits (uint16) for a bf16 cache
+    k_pages: np.ndarray       # fp16 | bf16 bits (uint16) | int8 | E4M3 codes (uint8)
+    v_pages: np.ndarray       #   [NP, Hkv, bs, D]
+    k_scale: Optional[np.ndarray]   # fp32 [NP, Hkv, bs] for int8 and fp8, else None
     v_scale: Optional[np.ndarray]
     block_table: np.ndarray   # int32 [B, MB], -1 past each sequence's last block
     seq_lens: np.ndarray      # int32 [B]
@@ -94,8 +110,7 @@ class Workload:
     def kv_bytes(self) -> int:
         c = self.config
         return kv_read_bytes(self.seq_lens, c.n_kv_heads, c.head_dim,
-                             1 if c.kv_dtype == "int8" else 2,
-                             4 if c.kv_dtype == "int8" else 0)
+                             ELEM_BYTES[c.kv_dtype], SCALE_BYTES[c.kv_dtype])
 
 
 def kv_read_bytes(seq_lens, n_kv_heads: int, head_dim: int, elem_bytes: int,
@@ -118,8 +133,12 @@ def other_bytes(config: Config) -> int:
             + c.batch * c.max_blocks_per_seq * 4 + c.batch * 4)
 
 
+_NAN = {np.dtype(np.float16): np.float16(np.nan), np.dtype(np.uint16): np.uint16(0x7FC0)}
+
+
 def _poison_unused_slots(w: Workload, n_used_pages: int) -> None:
-    """Fill every slot no valid token owns with NaN (fp16 values, int8 scales)."""
+    """Fill every slot no valid token owns with NaN (fp16 and bf16 values, int8 and fp8
+    row scales)."""
     bs = w.config.block_size
     for b in range(w.config.batch):
         length = int(w.seq_lens[b])
@@ -128,8 +147,8 @@ def _poison_unused_slots(w: Workload, n_used_pages: int) -> None:
         if nb and tail < bs:
             page = w.block_table[b, nb - 1]
             if w.k_scale is None:
-                w.k_pages[page, :, tail:, :] = np.float16(np.nan)
-                w.v_pages[page, :, tail:, :] = np.float16(np.nan)
+                w.k_pages[page, :, tail:, :] = _NAN[w.k_pages.dtype]
+                w.v_pages[page, :, tail:, :] = _NAN[w.v_pages.dtype]
             else:
                 w.k_scale[page, :, tail:] = np.float32(np.nan)
                 w.v_scale[page, :, tail:] = np.float32(np.nan)
@@ -137,11 +156,22 @@ def _poison_unused_slots(w: Workload, n_used_pages: int) -> None:
                           w.block_table[w.block_table >= 0], assume_unique=False)
     if unused.size:
         if w.k_scale is None:
-            w.k_pages[unused] = np.float16(np.nan)
-            w.v_pages[unused] = np.float16(np.nan)
+            w.k_pages[unused] = _NAN[w.k_pages.dtype]
+            w.v_pages[unused] = _NAN[w.v_pages.dtype]
         else:
             w.k_scale[unused] = np.float32(np.nan)
             w.v_scale[unused] = np.float32(np.nan)
+
+
+def _bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Draw bf16 values: keep the upper 16 bits of each fp32 word (uint16 patterns)."""
+    return (np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _finite_e4m3_codes(rng, shape) -> np.ndarray:
+    """Codes uniform over the 254 finite E4M3 codes (0x7F and 0xFF are NaN)."""
+    u = rng.integers(0, 254, size=shape, dtype=np.int16)
+    return (u + (u >= 0x7F)).astype(np.uint8)
 
 
 def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False,
@@ -179,7 +209,8 @@ def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False
         table[b, :nb] = perm[offset:offset + nb]
         offset += nb
 
-    q = rng.standard_normal((c.batch, c.n_q_heads, d), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((c.batch, c.n_q_heads, d), dtype=np.float32)
+    q = _bf16_bits(q) if c.kv_dtype == "bf16" else q.astype(np.float16)
     shape = (n_pages, hkv, bs, d)
     k_scale = v_scale = None
     if c.kv_dtype == "fp16":
@@ -200,6 +231,14 @@ def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False
         v_pages = rng.integers(-127, 128, size=shape, dtype=np.int8)
         k_scale = rng.uniform(0.005, 0.02, size=shape[:3]).astype(np.float32)
         v_scale = rng.uniform(0.005, 0.02, size=shape[:3]).astype(np.float32)
+    elif c.kv_dtype == "bf16":
+        k_pages = _bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+        v_pages = _bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    elif c.kv_dtype == "fp8":
+        k_pages = _finite_e4m3_codes(rng, shape)
+        v_pages = _finite_e4m3_codes(rng, shape)
+        k_scale = (rng.uniform(0.005, 0.02, size=shape[:3]) * (127 / 448)).astype(np.float32)
+        v_scale = (rng.uniform(0.005, 0.02, size=shape[:3]) * (127 / 448)).astype(np.float32)
     else:
         raise ValueError(f"unknown kv_dtype {c.kv_dtype!r}")
 

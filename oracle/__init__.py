@@ -13,3 +13,4 @@ from .decode import (  # noqa: F401
     kv_head_of,
 )
 from .append import append_kv, quantize_row  # noqa: F401
+from .formats import bf16_to_float64, e4m3_to_float64, element_values  # noqa: F401

@@ -20,6 +20,9 @@ What it computes, and where the pages define it:
 * Per-row INT8 (xLLM README, optimisation list, quantisation): a stored row is
   one (token, KV head) vector of int8 values with one fp32 scale; its value is
   int8 * scale.
+* BF16 caches (xLLM README, quantisation: "FP16, BF16") and FP8 E4M3 caches
+  with per-row scales (C++/CUDA engine blog, section 4): elements are decoded
+  to their exact values by ``oracle/formats.py`` before anything else.
 * The online-normaliser softmax (xLLM README, SoftMax operator) and the
   split/merge of PagedAttention v2 / Flash-Decoding (swiftLLM feature list)
   are ways to reach this same result faster. The oracle uses neither: it is
@@ -27,8 +30,9 @@ What it computes, and where the pages define it:
 
 Memory layout read here (the pages leave it open; this is the library's
 documented layout):
-  q           [B, Hq, D]            fp16
-  k_pages     [NP, Hkv, bs, D]      fp16, or int8 with k_scale [NP, Hkv, bs] fp32
+  q           [B, Hq, D]            fp16 (bf16 bit patterns, uint16, for a bf16 cache)
+  k_pages     [NP, Hkv, bs, D]      fp16; bf16 as uint16 bit patterns; or int8 or
+                                    E4M3 codes (uint8) with k_scale [NP, Hkv, bs] fp32
   v_pages     [NP, Hkv, bs, D]      same as k_pages
   block_table [B, MB]               int32; entry j of row b is the physical page
                                     holding tokens j*bs .. j*bs+bs-1 of sequence b
@@ -41,6 +45,8 @@ inputs, a float64 library attention routine, closed forms and invariants).
 from __future__ import annotations
 
 import numpy as np
+
+from .formats import element_values
 
 __all__ = [
     "gather_sequence",
@@ -76,8 +82,10 @@ def gather_sequence(pages: np.ndarray, table_row: np.ndarray, seq_len: int,
 def dequantize_rows(rows_int8: np.ndarray, row_scales: np.ndarray) -> np.ndarray:
     """Per-row INT8 (xLLM README, quantisation): value = int8 * row scale.
 
-    ``rows_int8`` is [..., D]; ``row_scales`` is [...] (one fp32 scale per
-    row). Symmetric, no zero point, no clamping. Returns float64.
+    ``rows_int8`` is [..., D] (int8 values, or the float64 values of decoded
+    E4M3 codes, which take their row scale the same way); ``row_scales`` is
+    [...] (one fp32 scale per row). Symmetric, no zero point, no clamping.
+    Returns float64.
     """
     return rows_int8.astype(np.float64) * row_scales.astype(np.float64)[..., None]
 
@@ -141,19 +149,17 @@ def decode_attention(q, k_pages, v_pages, block_table, seq_lens, scale,
     probs = {}
     for b in range(batch):
         length = int(seq_lens[b])
-        keys = gather_sequence(k_pages, block_table[b], length, block_size)
-        values = gather_sequence(v_pages, block_table[b], length, block_size)
+        keys = element_values(gather_sequence(k_pages, block_table[b], length, block_size))
+        values = element_values(gather_sequence(v_pages, block_table[b], length, block_size))
         if quantized:
             keys = dequantize_rows(
                 keys, gather_sequence(k_scale, block_table[b], length, block_size))
             values = dequantize_rows(
                 values, gather_sequence(v_scale, block_table[b], length, block_size))
-        else:
-            keys = keys.astype(np.float64)
-            values = values.astype(np.float64)
+        q_b = element_values(q[b])
         for h in range(n_q):
             g = kv_head_of(h, group)
-            o, l, p = attend(q[b, h].astype(np.float64), keys[g], values[g], sigma)
+            o, l, p = attend(q_b[h], keys[g], values[g], sigma)
             out[b, h] = o
             lse[b, h] = l
             if return_probs:

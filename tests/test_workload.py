@@ -95,3 +95,19 @@ def test_poison_marks_only_unowned_slots():
             valid[w.block_table[b, t // bs], :, t % bs] = True
     nan_rows = np.isnan(w.k_pages).all(axis=-1)
     assert np.array_equal(nan_rows, ~valid)
+
+
+def test_bf16_and_fp8_presets_draw_the_stated_values():
+    from decode_phase_attention_paged_amd.workload import CONFIGS
+    wb = generate(CONFIGS[6].with_(batch=4), seed=6)
+    assert wb.q.dtype == np.uint16 and wb.k_pages.dtype == np.uint16 and wb.k_scale is None
+    vals = (wb.k_pages.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(np.isfinite(vals)) and 0.9 < vals.std() < 1.1
+    wf = generate(CONFIGS[7].with_(batch=4), seed=7)
+    assert wf.k_pages.dtype == np.uint8 and wf.k_scale.dtype == np.float32
+    codes = np.concatenate([wf.k_pages.ravel(), wf.v_pages.ravel()])
+    assert not np.isin(codes, [0x7F, 0xFF]).any()
+    assert len(np.unique(codes)) == 254
+    assert wf.k_scale.min() >= 0.005 * 127 / 448 * 0.999 and wf.k_scale.max() <= 0.02 * 127 / 448
+    assert wf.kv_bytes == int(wf.seq_lens.sum()) * 32 * 2 * (128 + 4)
+    assert wb.kv_bytes == int(wb.seq_lens.sum()) * 32 * 2 * 256
