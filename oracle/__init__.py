@@ -12,5 +12,10 @@ from .decode import (  # noqa: F401
     gather_sequence,
     kv_head_of,
 )
-from .append import append_kv, quantize_row  # noqa: F401
-from .formats import bf16_to_float64, e4m3_to_float64, element_values  # noqa: F401
+from .append import append_kv, quantize_row, quantize_row_fp8  # noqa: F401
+from .formats import (  # noqa: F401
+    bf16_to_float64,
+    e4m3_from_float32,
+    e4m3_to_float64,
+    element_values,
+)

@@ -29,7 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["bf16_to_float64", "e4m3_to_float64", "element_values"]
+__all__ = ["bf16_to_float64", "e4m3_to_float64", "e4m3_from_float32", "element_values"]
 
 
 def bf16_to_float64(bits: np.ndarray) -> np.ndarray:
@@ -57,6 +57,24 @@ def e4m3_to_float64(codes: np.ndarray) -> np.ndarray:
     magnitude = np.where(exponent == 0, subnormal, normal)
     magnitude = np.where((exponent == 0xF) & ((c & 0x7) == 0x7), np.nan, magnitude)
     return sign * magnitude
+
+
+def e4m3_from_float32(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code to each fp32 value, ties to the even code (even last mantissa
+    bit), the sign kept (so -0.0 gives 0x80). Magnitudes above 448 saturate to 448: the
+    pages fix no overflow rule, and the quantiser below never produces one. NaN is not
+    accepted."""
+    v = np.asarray(v, dtype=np.float32)
+    if np.isnan(v).any():
+        raise ValueError("NaN has no E4M3 code here")
+    grid = e4m3_to_float64(np.arange(0x7F, dtype=np.uint8))   # codes 0..126, increasing
+    a = np.abs(v.astype(np.float64))
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, len(grid) - 1)
+    lo = np.clip(hi - 1, 0, len(grid) - 1)
+    d_hi, d_lo = np.abs(grid[hi] - a), np.abs(a - grid[lo])
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def element_values(x: np.ndarray) -> np.ndarray:

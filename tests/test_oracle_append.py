@@ -1,14 +1,16 @@
 """Pins for the K/V-append oracle (oracle/append.py), none of which re-types it:
-closed forms of the per-row INT8 rule, its rounding bound, a brute-force page
-walk on a flat pool, untouched-memory invariants, agreement with the attention
-oracle over the grown cache, and planted mistakes that must fail at least one
-pin."""
+closed forms of the per-row INT8 and FP8 rules, their rounding bounds, torch's
+own float32 -> float8_e4m3fn rounding, a brute-force page walk on a flat pool,
+untouched-memory invariants, agreement with the attention oracle over the grown
+cache, and planted mistakes that must fail at least one pin."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import append as app
+from oracle import formats as fmt
 
 
 F32 = np.float32
@@ -65,9 +67,92 @@ def test_rounding_error_bound_and_full_range():
         assert np.abs(codes).max() == 127
 
 
+# ------------------------------------------------------------------ per-row FP8 rule
+
+def torch_e4m3_codes(v):
+    return torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def e4m3_grid():
+    return torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_rounding_matches_torch():
+    rng = np.random.default_rng(11)
+    grid = e4m3_grid()
+    mids = (grid[1:] + grid[:-1]) / 2                      # every tie between neighbours
+    rand = rng.uniform(-1, 1, size=20000) * np.exp2(rng.uniform(-12, 8.8, size=20000))
+    v = np.concatenate([mids, -mids, grid, -grid, rand, [0.0, -0.0]]).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    assert np.array_equal(oracle.e4m3_from_float32(v), torch_e4m3_codes(v))
+
+
+def test_e4m3_codes_round_trip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(oracle.e4m3_from_float32(vals), codes)
+
+
+def test_fp8_single_element_maps_to_448():
+    for a in (1.0, -3.5, 1e-3, 6.0e4):
+        x = np.zeros(128, dtype=np.float16)
+        x[3] = a
+        codes, s = oracle.quantize_row_fp8(x)
+        assert s == F32(abs(F32(np.float16(a)))) / F32(448)
+        assert codes[3] == (0x7E if a > 0 else 0xFE)
+        assert np.count_nonzero(codes) == 1
+
+
+def test_fp8_zero_row_and_exact_rows():
+    codes, s = oracle.quantize_row_fp8(np.zeros(128, dtype=np.float16))
+    assert s == 0 and not codes.any() and codes.dtype == np.uint8
+    # Rows of E4M3 values times a power of two c, with one element at 448 c: s = c exactly,
+    # so the codes come back unchanged.
+    rng = np.random.default_rng(12)
+    grid = e4m3_grid()
+    for c in (2.0 ** -8, 2.0 ** -3, 1.0):
+        idx = rng.integers(0, 0x7F, size=128)
+        sign = rng.integers(0, 2, size=128)
+        idx[9], sign[9] = 0x7E, 1
+        x = (np.where(sign, -1, 1) * grid[idx] * c).astype(np.float16)
+        assert np.array_equal(x.astype(np.float64), np.where(sign, -1, 1) * grid[idx] * c)
+        codes, s = oracle.quantize_row_fp8(x)
+        assert s == F32(c)
+        want = (idx | np.where(sign, 0x80, 0)).astype(np.uint8)
+        nz = grid[idx] != 0
+        assert np.array_equal(codes[nz], want[nz])
+
+
+def test_fp8_rounding_error_bound():
+    # Nearest rounding: relative error at most 2^-4 in the normal range, absolute at most
+    # 2^-10 (half a subnormal step) below 2^-6, both in units of the row scale, plus the
+    # fp32 rounding of x / s.
+    rng = np.random.default_rng(13)
+    for _ in range(200):
+        x = (rng.standard_normal(128) * rng.uniform(0.01, 100)).astype(np.float16)
+        codes, s = oracle.quantize_row_fp8(x)
+        deq = fmt.e4m3_to_float64(codes) * float(s)
+        xa = x.astype(np.float64)
+        bound = np.maximum(np.abs(xa) * 2.0 ** -4, 2.0 ** -10 * float(s)) * (1 + 1e-6)
+        assert np.all(np.abs(deq - xa) <= bound)
+        assert np.abs(fmt.e4m3_to_float64(codes)).max() == 448
+
+
 # ------------------------------------------------------------------ page placement
 
-def small_cache(int8, rng, np_=7, hkv=2, bs=4, d=8):
+def small_cache(int8, rng, np_=7, hkv=2, bs=4, d=8, kind=None):
+    kind = kind or ("int8" if int8 else "fp16")
+    if kind == "fp8":
+        k = rng.integers(0, 0x7F, size=(np_, hkv, bs, d)).astype(np.uint8)
+        v = rng.integers(0x80, 0xFF, size=(np_, hkv, bs, d)).astype(np.uint8)
+        ks = rng.uniform(0.1, 1, size=(np_, hkv, bs)).astype(np.float32)
+        vs = rng.uniform(0.1, 1, size=(np_, hkv, bs)).astype(np.float32)
+        return k, v, ks, vs
+    if kind == "bf16":
+        k = rng.integers(0, 1 << 16, size=(np_, hkv, bs, d)).astype(np.uint16)
+        v = rng.integers(0, 1 << 16, size=(np_, hkv, bs, d)).astype(np.uint16)
+        return k, v, None, None
     if int8:
         k = rng.integers(-127, 128, size=(np_, hkv, bs, d)).astype(np.int8)
         v = rng.integers(-127, 128, size=(np_, hkv, bs, d)).astype(np.int8)
@@ -80,17 +165,24 @@ def small_cache(int8, rng, np_=7, hkv=2, bs=4, d=8):
     return k, v, ks, vs
 
 
-@pytest.mark.parametrize("int8", [False, True])
-def test_brute_force_on_a_flat_pool(int8):
+@pytest.mark.parametrize("kind", ["fp16", "int8", "bf16", "fp8"])
+def test_brute_force_on_a_flat_pool(kind):
     # The flat pool is addressed as ((page * Hkv + g) * bs + slot) * D + d, with
-    # page = table[b][p // bs] and slot = p % bs; rows with p < 0 are skipped.
+    # page = table[b][p // bs] and slot = p % bs; rows with p < 0 are skipped. FP8 codes
+    # come from torch's float32 -> float8_e4m3fn rounding of x / s.
     rng = np.random.default_rng(5)
-    k, v, ks, vs = small_cache(int8, rng)
+    int8 = kind in ("int8", "fp8")
+    k, v, ks, vs = small_cache(int8, rng, kind=kind)
     np_, hkv, bs, d = k.shape
     table = np.array([[6, 2, 0], [1, 4, 3], [5, 5, 5]], dtype=np.int32)
     positions = np.array([9, 3, -1], dtype=np.int32)      # page 0 slot 1; page 1 slot 3
-    k_new = rng.standard_normal((3, hkv, d)).astype(np.float16)
-    v_new = rng.standard_normal((3, hkv, d)).astype(np.float16)
+    if kind == "bf16":
+        k_new = rng.integers(0, 1 << 16, size=(3, hkv, d)).astype(np.uint16)
+        v_new = rng.integers(0, 1 << 16, size=(3, hkv, d)).astype(np.uint16)
+    else:
+        k_new = rng.standard_normal((3, hkv, d)).astype(np.float16)
+        v_new = rng.standard_normal((3, hkv, d)).astype(np.float16)
+    top = 448 if kind == "fp8" else 127
     got = oracle.append_kv(k, v, table, positions, k_new, v_new, bs, ks, vs)
 
     flat_k, flat_v = k.reshape(-1).copy(), v.reshape(-1).copy()
@@ -107,10 +199,18 @@ def test_brute_force_on_a_flat_pool(int8):
                 vals = [float(src[b, g, i]) for i in range(d)]
                 if int8:
                     m = max(abs(t) for t in vals)
-                    s = F32(F32(m) / F32(127))
+                    s = F32(F32(m) / F32(top))
                     flat_s[row] = s
                     for i in range(d):
-                        flat[row * d + i] = 0 if m == 0 else int(np.rint(F32(vals[i]) / s))
+                        if m == 0:
+                            flat[row * d + i] = 0
+                        elif kind == "fp8":
+                            flat[row * d + i] = torch_e4m3_codes([F32(vals[i]) / s])[0]
+                        else:
+                            flat[row * d + i] = int(np.rint(F32(vals[i]) / s))
+                elif kind == "bf16":
+                    for i in range(d):
+                        flat[row * d + i] = src[b, g, i]
                 else:
                     for i in range(d):
                         flat[row * d + i] = vals[i]
@@ -185,8 +285,13 @@ def pins_pass():
     tests = [test_single_nonzero_element_maps_to_127, test_zero_row_stores_zero_scale_and_codes,
              test_integer_multiples_of_a_power_of_two_are_exact, test_ties_round_to_even,
              test_rounding_error_bound_and_full_range,
-             lambda: test_brute_force_on_a_flat_pool(False),
-             lambda: test_brute_force_on_a_flat_pool(True),
+             lambda: test_brute_force_on_a_flat_pool("fp16"),
+             lambda: test_brute_force_on_a_flat_pool("int8"),
+             lambda: test_brute_force_on_a_flat_pool("bf16"),
+             lambda: test_brute_force_on_a_flat_pool("fp8"),
+             test_e4m3_rounding_matches_torch, test_e4m3_codes_round_trip,
+             test_fp8_single_element_maps_to_448, test_fp8_zero_row_and_exact_rows,
+             test_fp8_rounding_error_bound,
              test_inputs_untouched_and_only_target_rows_change]
     for t in tests:
         try:
@@ -240,6 +345,33 @@ def _append_swapped_kv(k_pages, v_pages, block_table, positions, k_new, v_new, b
                        k_scale, v_scale)
 
 
+def _fp8_max_240(x):
+    x32 = np.asarray(x, dtype=F32)
+    m = F32(np.max(np.abs(x32)))
+    if m == 0:
+        return np.zeros(x32.shape, dtype=np.uint8), F32(0)
+    s = F32(m / F32(240))
+    return fmt.e4m3_from_float32(x32 / s), s
+
+
+def _e4m3_ties_away(v):
+    v = np.asarray(v, dtype=np.float32)
+    grid = fmt.e4m3_to_float64(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(v.astype(np.float64))
+    hi = np.clip(np.searchsorted(grid, a), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    code = np.where(np.abs(grid[hi] - a) <= np.abs(a - grid[lo]), hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def _e4m3_truncate(v):
+    v = np.asarray(v, dtype=np.float32)
+    grid = fmt.e4m3_to_float64(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(v.astype(np.float64))
+    code = np.clip(np.searchsorted(grid, a, side="right") - 1, 0, 126).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
 ORIG_APPEND = app.append_kv
 
 
@@ -249,8 +381,13 @@ ORIG_APPEND = app.append_kv
     ("codes truncated", "quantize_row", _quantize_truncate),
     ("slot off by one", "append_kv", _append_wrong_slot),
     ("K and V swapped", "append_kv", _append_swapped_kv),
+    ("fp8 scale over 240", "quantize_row_fp8", _fp8_max_240),
+    ("fp8 ties away from zero", "e4m3_from_float32", _e4m3_ties_away),
+    ("fp8 codes truncated", "e4m3_from_float32", _e4m3_truncate),
 ])
 def test_planted_mistakes_fail_a_pin(monkeypatch, name, target, mutant):
     monkeypatch.setattr(app, target, mutant)
     monkeypatch.setattr(oracle, target, mutant)
+    if hasattr(fmt, target):
+        monkeypatch.setattr(fmt, target, mutant)
     assert not pins_pass(), f"planted mistake not caught: {name}"
