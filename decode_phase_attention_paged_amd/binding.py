@@ -23,6 +23,35 @@ LIB_PATH = os.path.join(_HERE, "libdecode_attn.so")
 
 KV_FP16 = 0
 KV_INT8 = 1
+KV_BF16 = 2
+KV_FP8 = 3
+KV_NAMES = {KV_FP16: "fp16", KV_INT8: "int8", KV_BF16: "bf16", KV_FP8: "fp8"}
+_KV_CODES = {v: k for k, v in KV_NAMES.items()}
+# Pool element type -> storage format; INT8 and FP8 rows carry fp32 scales.
+_KV_OF_DTYPE = {torch.float16: KV_FP16, torch.int8: KV_INT8, torch.bfloat16: KV_BF16,
+                torch.float8_e4m3fn: KV_FP8}
+_SCALED = (KV_INT8, KV_FP8)
+
+
+def _pool_format(k_pages, k_scale, v_scale):
+    """Storage format of the pools, with the scale checks that go with it."""
+    kv = _KV_OF_DTYPE.get(k_pages.dtype)
+    if kv is None:
+        raise ValueError("k_pages must be fp16, bf16, int8 or float8_e4m3fn")
+    if kv in _SCALED:
+        if k_scale is None or v_scale is None:
+            raise ValueError(f"{KV_NAMES[kv]} caches need k_scale and v_scale")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_pages.shape[:3]):
+                raise ValueError("row scales must be fp32 [num_pages, n_kv_heads, block_size]")
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("row scales are only for int8 and fp8 caches")
+    return kv
+
+
+def _row_dtype(kv):
+    """Type of q and of new K/V rows for a storage format: bf16 for a bf16 cache, else fp16."""
+    return torch.bfloat16 if kv == KV_BF16 else torch.float16
 STATUS = {0: "DECODE_ATTN_OK", 1: "DECODE_ATTN_ERR_INVALID_ARGUMENT",
           2: "DECODE_ATTN_ERR_UNSUPPORTED", 3: "DECODE_ATTN_ERR_WORKSPACE",
           4: "DECODE_ATTN_ERR_HIP"}
@@ -115,23 +144,12 @@ def _validate(q, k_pages, v_pages, block_table, seq_lens, k_scale, v_scale, out)
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if q.dtype != torch.float16 or q.dim() != 3:
-        raise ValueError("q must be fp16 [batch, n_q_heads, head_dim]")
     if k_pages.dim() != 4 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
         raise ValueError("k_pages and v_pages must both be [num_pages, n_kv_heads, block_size, head_dim]")
-    if k_pages.dtype == torch.float16:
-        kv = KV_FP16
-        if k_scale is not None or v_scale is not None:
-            raise ValueError("row scales are only for int8 caches")
-    elif k_pages.dtype == torch.int8:
-        kv = KV_INT8
-        if k_scale is None or v_scale is None:
-            raise ValueError("int8 caches need k_scale and v_scale")
-        for t in (k_scale, v_scale):
-            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_pages.shape[:3]):
-                raise ValueError("row scales must be fp32 [num_pages, n_kv_heads, block_size]")
-    else:
-        raise ValueError("k_pages must be fp16 or int8")
+    kv = _pool_format(k_pages, k_scale, v_scale)
+    if q.dtype != _row_dtype(kv) or q.dim() != 3:
+        raise ValueError(f"q must be {_row_dtype(kv)} [batch, n_q_heads, head_dim] for a "
+                         f"{KV_NAMES[kv]} cache")
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise ValueError("block_table must be int32 [batch, max_blocks_per_seq]")
     if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (q.shape[0],):
@@ -176,10 +194,10 @@ def plan(batch: int, max_blocks_per_seq: int, n_q_heads: int, n_kv_heads: int,
          block_size: int = 16, kv_dtype: str = "fp16", num_workgroups: int = 0,
          num_splits: int = 0, num_cus: int = 0) -> Plan:
     """The plan the library uses for these shapes and requests (see decode_attn_plan);
-    kv_dtype is "fp16" or "int8"."""
+    kv_dtype is "fp16", "bf16", "int8" or "fp8"."""
     lib = load_library()
     out = Plan()
-    kv = {"fp16": 0, "int8": 1}[kv_dtype]
+    kv = _KV_CODES[kv_dtype]
     _check(lib.decode_attn_plan(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size,
                                 kv, num_workgroups, num_splits, num_cus, ctypes.byref(out)),
            "decode_attn_plan")
@@ -209,7 +227,7 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
                 or not lse_out.is_contiguous() or lse_out.device != q.device):
             raise ValueError("lse_out must be contiguous fp32 [batch, n_q_heads] on q's device")
     cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-    need = plan(batch, mb, n_q, n_kv, bs, kv_dtype="int8" if kv == KV_INT8 else "fp16",
+    need = plan(batch, mb, n_q, n_kv, bs, kv_dtype=KV_NAMES[kv],
                 num_workgroups=num_workgroups, num_splits=num_splits,
                 num_cus=cus).workspace_bytes
     if workspace is None and need > 0:
@@ -227,10 +245,11 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
 
 def decode_attn_append(k_new, v_new, block_table, positions, k_pages, v_pages, *,
                        k_scale=None, v_scale=None):
-    """Write each sequence's new K/V row (fp16 [batch, n_kv_heads, head_dim]) into its
-    page slot, in place: row (b, g) goes to page block_table[b, p // bs], slot p % bs,
-    with p = positions[b] (int32; p < 0 skips b). INT8 pools (with k_scale / v_scale)
-    store per-row codes and scales (see decode_attn_append in include/decode_attn.h).
+    """Write each sequence's new K/V row (fp16 [batch, n_kv_heads, head_dim]; bf16 for a
+    bf16 cache) into its page slot, in place: row (b, g) goes to page
+    block_table[b, p // bs], slot p % bs, with p = positions[b] (int32; p < 0 skips b).
+    INT8 and FP8 pools (with k_scale / v_scale) store per-row codes and scales (see
+    decode_attn_append in include/decode_attn.h).
     The work is enqueued on torch's current stream of k_new's device."""
     lib = load_library()
     dev = k_new.device
@@ -247,24 +266,14 @@ def decode_attn_append(k_new, v_new, block_table, positions, k_pages, v_pages, *
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if k_new.dtype != torch.float16 or k_new.dim() != 3 or v_new.shape != k_new.shape \
-            or v_new.dtype != torch.float16:
-        raise ValueError("k_new and v_new must be fp16 [batch, n_kv_heads, head_dim]")
     if k_pages.dim() != 4 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
         raise ValueError("k_pages and v_pages must both be [num_pages, n_kv_heads, block_size, head_dim]")
-    if k_pages.dtype == torch.float16:
-        kv = KV_FP16
-        if k_scale is not None or v_scale is not None:
-            raise ValueError("row scales are only for int8 caches")
-    elif k_pages.dtype == torch.int8:
-        kv = KV_INT8
-        if k_scale is None or v_scale is None:
-            raise ValueError("int8 caches need k_scale and v_scale")
-        for t in (k_scale, v_scale):
-            if t.dtype != torch.float32 or tuple(t.shape) != tuple(k_pages.shape[:3]):
-                raise ValueError("row scales must be fp32 [num_pages, n_kv_heads, block_size]")
-    else:
-        raise ValueError("k_pages must be fp16 or int8")
+    kv = _pool_format(k_pages, k_scale, v_scale)
+    row = _row_dtype(kv)
+    if k_new.dtype != row or k_new.dim() != 3 or v_new.shape != k_new.shape \
+            or v_new.dtype != row:
+        raise ValueError(f"k_new and v_new must be {row} [batch, n_kv_heads, head_dim] for a "
+                         f"{KV_NAMES[kv]} cache")
     batch, n_kv, head_dim = k_new.shape
     num_pages, pool_kv, block_size, pool_d = k_pages.shape
     if (pool_kv, pool_d) != (n_kv, head_dim):

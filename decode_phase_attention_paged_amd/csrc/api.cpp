@@ -16,7 +16,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (5 << 16) | 0;
+constexpr int kVersion = (6 << 16) | 0;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -101,9 +101,10 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType k
     return p;
   }
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
-  // The segment-mode build for INT8 with G = 8 keeps too many registers live and spills, so
-  // the library's own plan only sends it there when the stream cannot take the batch.
-  const bool seg_spills = kv == dattn::KvType::kI8 && group == 8;
+  // The segment-mode builds for the 1-byte formats with G = 8 keep too many registers live
+  // and spill, so the library's own plan only sends them there when the stream cannot take
+  // the batch.
+  const bool seg_spills = dattn::kv_elem_bytes(kv) == 1 && group == 8;
   const bool seg_ok = !seg_spills || batch > dattn::kMaxBatch;
   // Segment mode needs a few segments per workgroup to balance whole segments, unless the
   // caches are short.
@@ -137,8 +138,23 @@ bool plan_needs_cus(int max_blocks, int requested_workgroups, int requested_spli
   return requested_workgroups == 0 && (requested_splits <= 1 || max_blocks == 1);
 }
 
+bool known_kv(int kv_dtype) {
+  return kv_dtype == DECODE_ATTN_KV_FP16 || kv_dtype == DECODE_ATTN_KV_INT8 ||
+         kv_dtype == DECODE_ATTN_KV_BF16 || kv_dtype == DECODE_ATTN_KV_FP8;
+}
+
+// Formats whose rows carry an fp32 scale.
+bool scaled_kv(int kv_dtype) {
+  return kv_dtype == DECODE_ATTN_KV_INT8 || kv_dtype == DECODE_ATTN_KV_FP8;
+}
+
 dattn::KvType kv_of(int kv_dtype) {
-  return kv_dtype == DECODE_ATTN_KV_INT8 ? dattn::KvType::kI8 : dattn::KvType::kF16;
+  switch (kv_dtype) {
+    case DECODE_ATTN_KV_INT8: return dattn::KvType::kI8;
+    case DECODE_ATTN_KV_BF16: return dattn::KvType::kBF16;
+    case DECODE_ATTN_KV_FP8: return dattn::KvType::kFP8;
+    default: return dattn::KvType::kF16;
+  }
 }
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -163,10 +179,9 @@ int validate(const void* q, const void* k_pages, const void* v_pages, const floa
                            requested_workgroups, requested_splits);
   if (st != DECODE_ATTN_OK) return st;
   if (num_pages < 1 || head_dim < 1) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  if (kv_dtype != DECODE_ATTN_KV_FP16 && kv_dtype != DECODE_ATTN_KV_INT8)
-    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  const bool int8 = kv_dtype == DECODE_ATTN_KV_INT8;
-  if (int8 != (k_scale != nullptr) || int8 != (v_scale != nullptr))
+  if (!known_kv(kv_dtype)) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  const bool scaled = scaled_kv(kv_dtype);
+  if (scaled != (k_scale != nullptr) || scaled != (v_scale != nullptr))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (batch > 0 && (q == nullptr || k_pages == nullptr || v_pages == nullptr ||
                     block_table == nullptr || seq_lens == nullptr || out == nullptr))
@@ -246,8 +261,7 @@ int decode_attn_plan(int batch, int max_blocks_per_seq, int n_q_heads, int n_kv_
                      int block_size, int kv_dtype, int requested_workgroups,
                      int requested_splits, int num_cus, decode_attn_plan_t* plan) {
   if (plan == nullptr || num_cus < 0) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  if (kv_dtype != DECODE_ATTN_KV_FP16 && kv_dtype != DECODE_ATTN_KV_INT8)
-    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (!known_kv(kv_dtype)) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   int st = validate_shapes(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size,
                            requested_workgroups, requested_splits);
   if (st != DECODE_ATTN_OK) return st;
@@ -344,10 +358,9 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
   if (batch < 0 || max_blocks_per_seq < 1 || num_pages < 1 || n_kv_heads < 1 ||
       head_dim < 1 || block_size < 1)
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  if (kv_dtype != DECODE_ATTN_KV_FP16 && kv_dtype != DECODE_ATTN_KV_INT8)
-    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  const bool int8 = kv_dtype == DECODE_ATTN_KV_INT8;
-  if (int8 != (k_scale != nullptr) || int8 != (v_scale != nullptr))
+  if (!known_kv(kv_dtype)) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  const bool scaled = scaled_kv(kv_dtype);
+  if (scaled != (k_scale != nullptr) || scaled != (v_scale != nullptr))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (batch > 0 && (k_new == nullptr || v_new == nullptr || block_table == nullptr ||
                     positions == nullptr || k_pages == nullptr || v_pages == nullptr))

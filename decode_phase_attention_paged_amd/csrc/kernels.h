@@ -17,7 +17,11 @@ constexpr int kPieceSlots = 2;    // partial results a stream worker can leave
 
 constexpr int kOrderMax = kThreads;  // batches up to this size run longest sequence first
 
-enum class KvType { kF16 = 0, kI8 = 1 };
+// Storage format of the K/V pools (and, for kBF16, of q). kI8 and kFP8 carry one fp32 scale
+// per (token, KV head) row.
+enum class KvType { kF16 = 0, kI8 = 1, kBF16 = 2, kFP8 = 3 };
+constexpr int kv_elem_bytes(KvType kv) { return kv == KvType::kF16 || kv == KvType::kBF16 ? 2 : 1; }
+constexpr bool kv_scaled(KvType kv) { return kv == KvType::kI8 || kv == KvType::kFP8; }
 
 // How the batch is cut into workgroups.
 //  kStream:  a fixed grid of persistent workgroups; the (sequence, KV head, page) units of
@@ -30,12 +34,13 @@ enum class Mode { kStream = 0, kSplit = 1, kSegment = 2 };
 
 constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
-// Waves per SIMD the segment-mode kernel is compiled for, by storage type and log2 G; the
-// host sizes that mode's grid to the workgroups that stay resident at that occupancy.
+// Waves per SIMD the segment-mode kernel is compiled for, by element width (2-byte and
+// 1-byte formats) and log2 G; the host sizes that mode's grid to the workgroups that stay
+// resident at that occupancy.
 constexpr int kSegWavesF16[4] = {3, 2, 2, 1};
 constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
 constexpr int seg_waves(KvType kv, int group) {
-  return kv == KvType::kF16 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];
+  return kv_elem_bytes(kv) == 2 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];
 }
 // Wavefronts of a segment-mode workgroup, which interleave the pages of its segment.
 constexpr int kSegW = 4;
@@ -45,10 +50,10 @@ constexpr int seg_workgroups_per_cu(KvType kv, int group) {
 }
 
 struct Args {
-  const void* q;               // fp16 [B, Hq, D]
-  const void* k_pages;         // fp16 | int8 [NP, Hkv, bs, D]
+  const void* q;               // fp16 [B, Hq, D] (bf16 for a bf16 cache)
+  const void* k_pages;         // fp16 | bf16 | int8 | fp8 e4m3 [NP, Hkv, bs, D]
   const void* v_pages;
-  const float* k_scale;        // fp32 [NP, Hkv, bs] (int8 only)
+  const float* k_scale;        // fp32 [NP, Hkv, bs] (int8 and fp8 only)
   const float* v_scale;
   const int32_t* block_table;  // int32 [B, MB]
   const int32_t* seq_lens;     // int32 [B]
@@ -87,13 +92,13 @@ hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStre
 
 // Appending a decode step's new K/V rows to the paged cache (append.hip).
 struct AppendArgs {
-  const void* k_new;           // fp16 [B, Hkv, D]
+  const void* k_new;           // fp16 [B, Hkv, D] (bf16 for a bf16 cache)
   const void* v_new;
   const int32_t* block_table;  // int32 [B, MB]
   const int32_t* positions;    // int32 [B]: token position of the new row, < 0 = none
-  void* k_pages;               // fp16 | int8 [NP, Hkv, bs, D]
+  void* k_pages;               // fp16 | bf16 | int8 | fp8 e4m3 [NP, Hkv, bs, D]
   void* v_pages;
-  float* k_scale;              // fp32 [NP, Hkv, bs] (int8 only)
+  float* k_scale;              // fp32 [NP, Hkv, bs] (int8 and fp8 only)
   float* v_scale;
   int batch;
   int max_blocks;              // MB

@@ -49,6 +49,7 @@ constexpr int kSplitTable = 1024;   // table entries a split workgroup stages in
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
 // Lane geometry. A lane owns one 16-byte chunk of one token row per load instruction.
@@ -56,24 +57,25 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 //       contiguous bytes [1024 i, 1024 i + 1024), lane l at byte 16 l.
 // int8: a row is 128 B = 8 lanes; lane row r covers tokens 2r and 2r + 1 (loads 0 and 1)
 //       so that its two row scales are one 8-byte load.
+// bf16 takes the fp16 geometry and fp8 the int8 one.
 template <KvType kKv>
 struct Geo {
-  static constexpr int kElem = kKv == KvType::kF16 ? 2 : 1;
+  static constexpr int kElem = kv_elem_bytes(kKv);
   static constexpr int kChunk = 16 / kElem;                 // elements per lane per load
   static constexpr int kLanesPerRow = kHeadDim / kChunk;    // 16 | 8
   static constexpr int kRows = kWave / kLanesPerRow;        // lane rows: 4 | 8
   static constexpr int kLoads = kBlockSize / kRows;         // loads per tile: 4 | 2
   static constexpr int kRowBytes = kHeadDim * kElem;
   static constexpr int kTileBytes = kBlockSize * kRowBytes;
-  static constexpr bool kScaled = kKv == KvType::kI8;
-  static constexpr int kPairs = kChunk / 2;                 // fp16 pairs per lane per load
+  static constexpr bool kScaled = kv_scaled(kKv);
+  static constexpr int kPairs = kChunk / 2;                 // element pairs per lane per load
 
   __device__ static int offset(int lane, int i) {
-    if constexpr (kKv == KvType::kF16) return i * 1024 + lane * 16;
+    if constexpr (kElem == 2) return i * 1024 + lane * 16;
     else return (lane / kLanesPerRow) * 256 + i * 128 + (lane % kLanesPerRow) * 16;
   }
   __device__ static int token(int row, int i) {
-    if constexpr (kKv == KvType::kF16) return i * kRows + row;
+    if constexpr (kElem == 2) return i * kRows + row;
     else return 2 * row + i;
   }
 };
@@ -98,23 +100,23 @@ constexpr int kSegDepthI8[4] = {1, 3, 2, 1};
 
 template <KvType kKv, int kGroup>
 constexpr int stream_depth() {
-  return kKv == KvType::kF16 ? kStreamDepthF16[log2_group(kGroup)] : kStreamDepthI8[log2_group(kGroup)];
+  return kv_elem_bytes(kKv) == 2 ? kStreamDepthF16[log2_group(kGroup)] : kStreamDepthI8[log2_group(kGroup)];
 }
 template <KvType kKv, int kGroup>
 constexpr int stream_waves() {
-  return kKv == KvType::kF16 ? kStreamWavesF16[log2_group(kGroup)] : kStreamWavesI8[log2_group(kGroup)];
+  return kv_elem_bytes(kKv) == 2 ? kStreamWavesF16[log2_group(kGroup)] : kStreamWavesI8[log2_group(kGroup)];
 }
 template <KvType kKv, int kGroup>
 constexpr int split_depth() {
-  return kKv == KvType::kF16 ? kSplitDepthF16[log2_group(kGroup)] : kSplitDepthI8[log2_group(kGroup)];
+  return kv_elem_bytes(kKv) == 2 ? kSplitDepthF16[log2_group(kGroup)] : kSplitDepthI8[log2_group(kGroup)];
 }
 template <KvType kKv, int kGroup>
 constexpr int split_waves() {
-  return kKv == KvType::kF16 ? kSplitWavesF16[log2_group(kGroup)] : kSplitWavesI8[log2_group(kGroup)];
+  return kv_elem_bytes(kKv) == 2 ? kSplitWavesF16[log2_group(kGroup)] : kSplitWavesI8[log2_group(kGroup)];
 }
 template <KvType kKv, int kGroup>
 constexpr int seg_depth() {
-  return kKv == KvType::kF16 ? kSegDepthF16[log2_group(kGroup)] : kSegDepthI8[log2_group(kGroup)];
+  return kv_elem_bytes(kKv) == 2 ? kSegDepthF16[log2_group(kGroup)] : kSegDepthI8[log2_group(kGroup)];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -146,6 +148,11 @@ __device__ __forceinline__ float row_sum(float v) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+__device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
+
+// The two bf16 values of a dword as exact fp32: a bf16 is the upper half of an fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
 // Four int8 values (one dword, lowest address in the low byte) to two exact fp16 pairs.
 // Each byte is biased to x + 128 and placed as the low mantissa byte of 1024.0h, which
@@ -159,14 +166,69 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
   hi = as_h2(c) - bias;
 }
 
+// Four E4M3 codes (one dword, lowest address in the low byte) to two fp16 pairs. Every
+// finite E4M3 value is exact in fp16 (magnitudes 2^-9 .. 448), and the hardware conversion
+// (unit scale) maps the NaN codes to NaN.
+__device__ __forceinline__ void fp8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
+// A load's elements as exact fp16 pairs (fp16, int8 and fp8 storage; bf16 values are not
+// all fp16 values and take their own path).
 template <KvType kKv>
 __device__ __forceinline__ void unpack(const u32x4& raw, h2 (&x)[Geo<kKv>::kPairs]) {
+  static_assert(kKv != KvType::kBF16, "bf16 is not unpacked to fp16");
   if constexpr (kKv == KvType::kF16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = as_h2(raw[e]);
-  } else {
+  } else if constexpr (kKv == KvType::kI8) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) i8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) fp8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
+  }
+}
+
+// q . k over this lane's elements of one load, accumulated in fp32 onto d. The query pairs
+// hold the query's raw 16-bit patterns: fp16 for every format but bf16, whose q is bf16.
+template <KvType kKv>
+__device__ __forceinline__ float dot_row(const u32x4& raw, const h2 (&q)[Geo<kKv>::kPairs]) {
+  float d = 0.0f;
+  if constexpr (kKv == KvType::kBF16) {
+#pragma unroll
+    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+      const uint32_t word = raw[e];
+      d = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(word), __builtin_bit_cast(bf2, q[e]), d, false);
+    }
+  } else {
+    h2 kx[Geo<kKv>::kPairs];
+    unpack<kKv>(raw, kx);
+#pragma unroll
+    for (int e = 0; e < Geo<kKv>::kPairs; ++e) d = __builtin_amdgcn_fdot2(kx[e], q[e], d, false);
+  }
+  return d;
+}
+
+// acc[j] += w * v[j] over this lane's elements of one load.
+template <KvType kKv>
+__device__ __forceinline__ void axpy_row(const u32x4& raw, float w, float (&acc)[Geo<kKv>::kChunk]) {
+  if constexpr (kKv == KvType::kBF16) {
+#pragma unroll
+    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+      const uint32_t word = raw[e];
+      acc[2 * e] = fmaf(w, bf16_lo(word), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(w, bf16_hi(word), acc[2 * e + 1]);
+    }
+  } else {
+    h2 vx[Geo<kKv>::kPairs];
+    unpack<kKv>(raw, vx);
+#pragma unroll
+    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+      acc[2 * e] = fmaf(w, static_cast<float>(vx[e].x), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(w, static_cast<float>(vx[e].y), acc[2 * e + 1]);
+    }
   }
 }
 
@@ -280,15 +342,11 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGro
   float s[kGroup][Gm::kLoads];
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) {
-    h2 kx[Gm::kPairs];
-    unpack<kKv>(t.k[i], kx);
     float f = scale_log2;
     if constexpr (Gm::kScaled) f *= t.ks[i];
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      float d = 0.0f;
-#pragma unroll
-      for (int e = 0; e < Gm::kPairs; ++e) d = __builtin_amdgcn_fdot2(kx[e], qh[h][e], d, false);
+      const float d = dot_row<kKv>(t.k[i], qh[h]);
       const float sc = row_sum<Gm::kLanesPerRow>(d) * f;
       s[h][i] = ok[i] ? sc : kNegInf;
     }
@@ -317,19 +375,13 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGro
   for (int i = 0; i < Gm::kLoads; ++i) {
     u32x4 raw = t.v[i];
     if constexpr (kMasked) raw = ok[i] ? raw : u32x4{0u, 0u, 0u, 0u};
-    h2 vx[Gm::kPairs];
-    unpack<kKv>(raw, vx);
     float vscale = 1.0f;
     if constexpr (Gm::kScaled) vscale = ok[i] ? t.vs[i] : 0.0f;
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       float pw = p[h][i];
       if constexpr (Gm::kScaled) pw *= vscale;
-#pragma unroll
-      for (int e = 0; e < Gm::kPairs; ++e) {
-        st.acc[h][2 * e] = fmaf(pw, static_cast<float>(vx[e].x), st.acc[h][2 * e]);
-        st.acc[h][2 * e + 1] = fmaf(pw, static_cast<float>(vx[e].y), st.acc[h][2 * e + 1]);
-      }
+      axpy_row<kKv>(raw, pw, st.acc[h]);
     }
   }
 }
@@ -1401,8 +1453,13 @@ void bind_workspace(Args& a, const Plan& plan, void* workspace) {
 }
 
 hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStream_t stream) {
-  return kv == KvType::kF16 ? launch_kv<KvType::kF16>(group, a, plan, stream)
-                            : launch_kv<KvType::kI8>(group, a, plan, stream);
+  switch (kv) {
+    case KvType::kF16: return launch_kv<KvType::kF16>(group, a, plan, stream);
+    case KvType::kI8: return launch_kv<KvType::kI8>(group, a, plan, stream);
+    case KvType::kBF16: return launch_kv<KvType::kBF16>(group, a, plan, stream);
+    case KvType::kFP8: return launch_kv<KvType::kFP8>(group, a, plan, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dattn

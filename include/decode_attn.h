@@ -6,8 +6,10 @@
  * LLM-Inferenz-Engine von Grund auf mit C++ und CUDA bauen", section 1.1). The cache
  * lives in fixed-size pages found through a per-sequence block table (swiftLLM README,
  * feature list: PagedAttention). Several query heads may share one KV head (xLLM README,
- * optimisation list: GQA), and the cache may be stored as per-row INT8 (xLLM README,
- * quantisation list). For sequence b and query head h, with G = n_q_heads / n_kv_heads
+ * optimisation list: GQA). The cache is stored as fp16 or bf16 (the precisions the xLLM
+ * README's quantisation list names), as per-row INT8 (same list), or as FP8 E4M3 with
+ * per-row scales (FP8 cache quantisation is among the next steps in section 4 of the
+ * C++/CUDA engine page). For sequence b and query head h, with G = n_q_heads / n_kv_heads
  * and g = h / G:
  *
  *     s_t = scale * <q[b,h,:], K_b[g,t,:]>        for t in [0, L_b)
@@ -33,12 +35,13 @@
  * Memory layout (all row-major and contiguous; all tensor pointers are DEVICE pointers
  * owned by the caller, for example torch tensors; the library never frees them):
  *
- *     q            fp16  [batch, n_q_heads, head_dim], 16-byte aligned
- *     k_pages      fp16 or int8  [num_pages, n_kv_heads, block_size, head_dim], 16-byte
+ *     q            fp16  [batch, n_q_heads, head_dim] (bf16 for a BF16 cache), 16-byte
  *                  aligned
+ *     k_pages      fp16, bf16, int8 or FP8 E4M3 codes  [num_pages, n_kv_heads, block_size,
+ *                  head_dim], 16-byte aligned
  *     v_pages      same type and shape as k_pages
- *     k_scale      fp32  [num_pages, n_kv_heads, block_size]   (INT8 only, else NULL;
- *     v_scale      fp32  [num_pages, n_kv_heads, block_size]    8-byte aligned)
+ *     k_scale      fp32  [num_pages, n_kv_heads, block_size]   (INT8 and FP8 only, else
+ *     v_scale      fp32  [num_pages, n_kv_heads, block_size]    NULL; 8-byte aligned)
  *     block_table  int32 [batch, max_blocks_per_seq]: entry (b, j) is the physical page
  *                  holding tokens j*block_size .. j*block_size+block_size-1 of sequence b.
  *                  Only entries j < ceil(L_b / block_size) are read; the rest may hold
@@ -50,7 +53,10 @@
  *
  * A (page, KV head) tile is block_size * head_dim contiguous elements (4 KiB in fp16 at
  * 16 x 128), so one page of one head is read with fully coalesced 16-byte loads. An INT8
- * row (token, KV head) has value int8 * scale with one fp32 scale per row; the slots of
+ * row (token, KV head) has value int8 * scale with one fp32 scale per row, and an FP8 row
+ * value e4m3(code) * scale the same way. BF16 is the upper half of an IEEE binary32. FP8
+ * is E4M3 as the OCP 8-bit floating-point specification defines it: bias 7, subnormals at
+ * exponent field 0, no infinities, S.1111.111 is NaN, largest magnitude 448. The slots of
  * a page past L_b are never used, whatever they hold (NaN included).
  *
  * Supported sizes: head_dim 128, block_size 16, G = n_q_heads / n_kv_heads in
@@ -93,7 +99,10 @@ typedef enum {
 /* Storage type of k_pages / v_pages. */
 typedef enum {
   DECODE_ATTN_KV_FP16 = 0,
-  DECODE_ATTN_KV_INT8 = 1 /* per-row INT8 with fp32 row scales (xLLM README, quantisation) */
+  DECODE_ATTN_KV_INT8 = 1, /* per-row INT8 with fp32 row scales (xLLM README, quantisation) */
+  DECODE_ATTN_KV_BF16 = 2, /* bf16 K/V and bf16 q (xLLM README, quantisation: FP16, BF16) */
+  DECODE_ATTN_KV_FP8 = 3   /* OCP E4M3 codes with fp32 row scales; q fp16 (C++/CUDA engine
+                              page, section 4: FP8 cache quantisation) */
 } decode_attn_kv_dtype;
 
 /* How a call cuts the batch into work (see the top of this file). */
@@ -182,19 +191,23 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
  * lives in page block_table[b, p / block_size], slot p % block_size (swiftLLM feature
  * list: PagedAttention).
  *
- *     k_new, v_new  fp16 [batch, n_kv_heads, head_dim], 16-byte aligned: the new rows.
+ *     k_new, v_new  fp16 [batch, n_kv_heads, head_dim] (bf16 for a BF16 cache), 16-byte
+ *                   aligned: the new rows.
  *     positions     int32 [batch]: the new token's position p_b in sequence b (its
  *                   length before the step); p_b < 0 means no new token for b.
  *     block_table   as for decode_attn; entry (b, p_b / block_size) must name the page
  *                   that receives the row (the caller allocates pages).
- *     k_pages, v_pages (and k_scale, v_scale for INT8) as for decode_attn, written in
+ *     k_pages, v_pages (and k_scale, v_scale for INT8 and FP8) as for decode_attn, written in
  *                   place: row (b, g) goes to [page, g, p_b % block_size]. Nothing else
  *                   in the pools is touched.
  *
- * FP16 pools store the row unchanged. INT8 pools (xLLM README, quantisation list:
- * per-row INT8) store symmetric codes: s = max_d |x_d| / 127 and code_d = rint(x_d / s)
- * (round half to even), both in fp32 with IEEE division, clamped to [-127, 127]; a row of
- * zeros stores s = 0 and codes 0. Rows must be finite.
+ * FP16 and BF16 pools store the row unchanged. INT8 pools (xLLM README, quantisation
+ * list: per-row INT8) store symmetric codes: s = max_d |x_d| / 127 and
+ * code_d = rint(x_d / s) (round half to even), both in fp32 with IEEE division, clamped
+ * to [-127, 127]. FP8 pools (E4M3, section 4 of the C++/CUDA engine page) store
+ * s = max_d |x_d| / 448 and code_d = the E4M3 code nearest to x_d / s (ties to the even
+ * code; the sign of a zero is kept), with the same fp32 divisions. A row of zeros stores
+ * s = 0 and codes 0. Rows must be finite.
  *
  * Bad device values never fault: a row whose position is at or past
  * max_blocks_per_seq * block_size, or whose table entry lies outside [0, num_pages), is
@@ -211,7 +224,7 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);
 
-/* Library ABI version: (major << 16) | minor. */
+/* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats. */
 int decode_attn_version(void);
 
 #ifdef __cplusplus

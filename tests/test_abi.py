@@ -51,7 +51,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 5
+    assert lib.decode_attn_version() >> 16 == 6
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -89,7 +89,11 @@ def call_ex(lib, wgs, splits, ws, ws_bytes, **over):
     (dict(kv=1), 1),                   # int8 without row scales
     (dict(ks=7 * A, vs=8 * A), 1),     # fp16 with row scales
     (dict(kv=1, ks=7 * A), 1),         # int8 with only one scale array
+    (dict(kv=3), 1),                   # fp8 without row scales
+    (dict(kv=3, vs=8 * A), 1),         # fp8 with only one scale array
+    (dict(kv=2, ks=7 * A, vs=8 * A), 1),   # bf16 with row scales
     (dict(kv=5), 1),                   # unknown storage type
+    (dict(kv=-1), 1),
     (dict(q=None), 1),
     (dict(out=None), 1),
     (dict(bt=None), 1),
@@ -210,7 +214,7 @@ def test_plan_rejects_bad_arguments(lib, binding):
     assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, -2, 0, 256, ctypes.byref(p)) == 1
     assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 2, 2, 256, ctypes.byref(p)) == 1
     assert lib.decode_attn_plan(1, 8, 6, 4, 16, 0, 0, 0, 256, ctypes.byref(p)) == 1
-    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 2, 0, 0, 256, ctypes.byref(p)) == 1   # kv type
+    assert lib.decode_attn_plan(1, 8, 8, 8, 16, 4, 0, 0, 256, ctypes.byref(p)) == 1   # kv type
     assert lib.decode_attn_plan(1, 8, 8, 8, 16, 0, 0, 0, 256, None) == 1
 
 
@@ -243,7 +247,9 @@ def call_append(lib, **over):
 @pytest.mark.parametrize("over,status", [
     (dict(kv=1), 1),                         # int8 without row scales
     (dict(ks=7 * A, vs=8 * A), 1),           # fp16 with row scales
-    (dict(kv=3), 1),
+    (dict(kv=3), 1),                         # fp8 without row scales
+    (dict(kv=2, ks=7 * A, vs=8 * A), 1),     # bf16 with row scales
+    (dict(kv=4), 1),                         # unknown storage type
     (dict(k=None), 1),
     (dict(kp=None), 1),
     (dict(pos=None), 1),

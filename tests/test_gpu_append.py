@@ -29,11 +29,38 @@ def lib(torch):
 
 
 def dev(torch, a):
-    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    """Host array to GPU tensor: bf16 bit patterns (uint16) as bfloat16, E4M3 codes (uint8)
+    as float8_e4m3fn."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    t = torch.from_numpy(a).to("cuda:0")
+    return t.view(torch.float8_e4m3fn) if a.dtype == np.uint8 else t
 
 
 def host(t):
-    return None if t is None else t.cpu().numpy()
+    """GPU tensor back to the host array layout the oracle uses."""
+    if t is None:
+        return None
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def new_rows(rng, kv, shape, spread=True):
+    """New K/V rows: fp16 N(0, 1) times a per-row U(0.1, 10), or bf16 bit patterns of the
+    same for a bf16 cache."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    if spread:
+        x *= rng.uniform(0.1, 10, size=shape[:2] + (1,)).astype(np.float32)
+    if kv == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)
+    return x.astype(np.float16)
 
 
 def grown_cache(cfg, seed, rng, extra_pages=3):
@@ -52,19 +79,18 @@ def grown_cache(cfg, seed, rng, extra_pages=3):
             need += 1
     if need:
         shape = (need,) + w.k_pages.shape[1:]
-        if cfg.kv_dtype == "int8":
-            add = [rng.integers(-127, 128, size=shape).astype(np.int8) for _ in range(2)]
+        if w.k_scale is not None:
+            add = [rng.integers(0, 127, size=shape).astype(w.k_pages.dtype) for _ in range(2)]
             scales = [np.concatenate([s, rng.uniform(0.01, 0.02, size=shape[:3]).astype(np.float32)])
                       for s in scales]
         else:
-            add = [rng.standard_normal(shape).astype(np.float16) for _ in range(2)]
+            add = [rng.integers(0, 1 << 14, size=shape).astype(w.k_pages.dtype) for _ in range(2)]
         pools = [np.concatenate([p, a]) for p, a in zip(pools, add)]
-    new = [(rng.standard_normal((cfg.batch, cfg.n_kv_heads, cfg.head_dim)) *
-            rng.uniform(0.1, 10, size=(cfg.batch, cfg.n_kv_heads, 1))).astype(np.float16)
-           for _ in range(2)]
-    new[0][0, 0] = 0.0                       # a zero row
-    new[1][0, 0] = 0.0
-    new[1][0, 0, 5] = -3.0                   # a single-element row
+    shape = (cfg.batch, cfg.n_kv_heads, cfg.head_dim)
+    new = [new_rows(rng, cfg.kv_dtype, shape) for _ in range(2)]
+    new[0][0, 0] = 0                         # a zero row
+    new[1][0, 0] = 0
+    new[1][0, 0, 5] = 0xC040 if cfg.kv_dtype == "bf16" else -3.0   # a single-element row: -3
     return w, table, lens, pools, scales, new
 
 
@@ -76,11 +102,15 @@ def run_append(torch, lib, table, positions, pools, scales, new):
     return host(d[2]), host(d[3]), host(ks), host(vs)
 
 
-CASES = [("small_fp16", 1, dict(batch=5, n_q_heads=6, n_kv_heads=3, len_lo=0, len_hi=70)),
-         ("small_int8", 1, dict(batch=5, n_q_heads=6, n_kv_heads=3, len_lo=0, len_hi=70,
-                                kv_dtype="int8")),
+SMALL_OVER = dict(batch=5, n_q_heads=6, n_kv_heads=3, len_lo=0, len_hi=70)
+CASES = [("small_fp16", 1, SMALL_OVER),
+         ("small_int8", 1, dict(SMALL_OVER, kv_dtype="int8")),
+         ("small_bf16", 1, dict(SMALL_OVER, kv_dtype="bf16")),
+         ("small_fp8", 1, dict(SMALL_OVER, kv_dtype="fp8")),
          ("llama2_7b_mha_b48", 2, {}),
-         ("int8_mha_b200", 5, {})]
+         ("int8_mha_b200", 5, {}),
+         ("llama2_7b_mha_b48_bf16", 6, {}),
+         ("fp8_mha_b200", 7, {})]
 
 
 @pytest.mark.parametrize("name,index,over", CASES, ids=[c[0] for c in CASES])
@@ -111,7 +141,7 @@ def test_append_is_bit_exact(torch, lib, name, index, over):
         assert bad.size == 0, f"{what}: {len(bad)} elements differ, first at {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("kv", ["fp16", "int8", "bf16", "fp8"])
 def test_three_steps_then_attention(torch, lib, kv):
     # Three decode steps: append at L_b, L_b + 1, L_b + 2 (crossing page boundaries for some
     # sequences), then attend over L_b + 3 tokens; the GPU pools stay bit-identical to the
@@ -135,7 +165,7 @@ def test_three_steps_then_attention(torch, lib, kv):
     if extra:
         shape = (extra,) + w.k_pages.shape[1:]
         pools = [np.concatenate([p, np.zeros(shape, dtype=p.dtype)]) for p in pools]
-        if kv == "int8":
+        if w.k_scale is not None:
             scales = [np.concatenate([s, np.zeros(shape[:3], dtype=np.float32)]) for s in scales]
     d_tab = dev(torch, table)
     d_k, d_v = dev(torch, pools[0]), dev(torch, pools[1])
@@ -143,7 +173,7 @@ def test_three_steps_then_attention(torch, lib, kv):
     ref = [pools[0], pools[1], scales[0], scales[1]]
     for step in range(3):
         pos = (lens + step).astype(np.int32)
-        new = [rng.standard_normal((cfg.batch, cfg.n_kv_heads, 128)).astype(np.float16)
+        new = [new_rows(rng, kv, (cfg.batch, cfg.n_kv_heads, 128), spread=False)
                for _ in range(2)]
         lib.decode_attn_append(dev(torch, new[0]), dev(torch, new[1]), d_tab, dev(torch, pos),
                                d_k, d_v, k_scale=d_ks, v_scale=d_vs)
@@ -151,7 +181,7 @@ def test_three_steps_then_attention(torch, lib, kv):
                                     cfg.block_size, ref[2], ref[3]))
     torch.cuda.synchronize()
     assert np.array_equal(host(d_k), ref[0]) and np.array_equal(host(d_v), ref[1])
-    if kv == "int8":
+    if w.k_scale is not None:
         assert np.array_equal(host(d_ks), ref[2]) and np.array_equal(host(d_vs), ref[3])
     grown = (lens + 3).astype(np.int32)
     out = lib.decode_attn(dev(torch, w.q), d_k, d_v, d_tab, dev(torch, grown), w.scale,

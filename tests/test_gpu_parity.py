@@ -30,9 +30,20 @@ def lib(torch):
     return binding
 
 
+def dev_tensor(torch, a):
+    """A host array on the GPU; bf16 bit patterns (uint16) become bfloat16 tensors and E4M3
+    codes (uint8) float8_e4m3fn tensors."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    t = torch.from_numpy(a).to("cuda:0")
+    return t.view(torch.float8_e4m3fn) if a.dtype == np.uint8 else t
+
+
 def to_dev(torch, w):
-    dev = torch.device("cuda:0")
-    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    t = lambda a: dev_tensor(torch, a)
     return dict(q=t(w.q), k_pages=t(w.k_pages), v_pages=t(w.v_pages), k_scale=t(w.k_scale),
                 v_scale=t(w.v_scale), block_table=t(w.block_table), seq_lens=t(w.seq_lens))
 
@@ -84,7 +95,10 @@ PLANS = [dict(), dict(num_workgroups=1), dict(num_workgroups=3), dict(num_workgr
 PLAN_IDS = ["auto", "wg1", "wg3", "wg64", "seg", "seg-wg1", "seg-wg2", "split3"]
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+KVS = ["fp16", "int8", "bf16", "fp8"]
+
+
+@pytest.mark.parametrize("kv", KVS)
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("plan", PLANS, ids=PLAN_IDS)
 def test_small_all_variants(torch, lib, kv, group, plan):
@@ -117,7 +131,7 @@ EDGE_PLANS = [dict(num_workgroups=1), dict(num_workgroups=4), dict(num_workgroup
               dict(num_splits=1, num_workgroups=5), dict(num_splits=4), dict(num_splits=19)]
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("kv", KVS)
 def test_edge_lengths_and_nan_canaries(torch, lib, kv):
     # Empty, single-token, page-boundary and full caches in one batch; every slot no token
     # owns (and 5 pages nobody references) holds NaN.
@@ -157,7 +171,7 @@ def test_segment_mode_order_and_grids(torch, lib, batch, grid, caches):
     assert_lse(lse, ref_lse, "lse")
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("kv", KVS)
 def test_stream_mode_query_rows_beyond_lds(torch, lib, kv):
     # Stream mode stages a workgroup's query rows in LDS when they fit in 16 KiB; one
     # workgroup over 80 (sequence, KV head) segments of G = 8 (2 KiB of query rows each)
@@ -187,7 +201,7 @@ def test_split_mode_partitions_beyond_one_table_chunk(torch, lib, longest):
     assert_lse(lse, ref_lse, "lse")
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("kv", KVS)
 def test_segment_mode_long_caches(torch, lib, kv):
     # Eight (sequence, KV head) segments of up to 9000 tokens (563 pages) on one, two or
     # eight workgroups: long runs of pages per wave across several segments, including a
@@ -203,7 +217,7 @@ def test_segment_mode_long_caches(torch, lib, kv):
         assert_lse(lse, ref_lse, "lse")
 
 
-@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("kv", KVS)
 @pytest.mark.parametrize("group", [1, 4, 8])
 def test_segment_mode_restages_query_rows(torch, lib, kv, group):
     # One or two workgroups over 90 (sequence, KV head) segments: more than one LDS chunk of
@@ -298,6 +312,48 @@ def test_int8_unit_scales_match_fp16_on_same_integers(torch, lib):
     np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-5)
 
 
+def test_fp8_small_integers_match_int8_bitwise(torch, lib):
+    # E4M3 codes whose values are the integers -16..16 decode to the same exact fp16 pairs
+    # as those integers stored as INT8, so with the same row scales both paths do identical
+    # arithmetic.
+    table = oracle.e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    code_of = {int(v): c for c, v in enumerate(table)
+               if np.isfinite(v) and v == int(v) and abs(v) <= 16 and not (v == 0 and c)}
+    cfg = SMALL.with_(kv_dtype="int8", n_q_heads=8, n_kv_heads=2)
+    w = generate(cfg, seed=17)
+    rng = np.random.default_rng(17)
+    ints = [rng.integers(-16, 17, size=w.k_pages.shape) for _ in range(2)]
+    w.k_pages, w.v_pages = (i.astype(np.int8) for i in ints)
+    for plan in (dict(), dict(num_workgroups=3), dict(num_splits=1), dict(num_splits=3)):
+        a, la = gpu_run(torch, lib, w, **plan)
+        w8 = generate(cfg, seed=17)
+        w8.k_pages, w8.v_pages = (np.vectorize(code_of.get)(i).astype(np.uint8) for i in ints)
+        b, lb = gpu_run(torch, lib, w8, **plan)
+        assert np.array_equal(a, b) and np.array_equal(la, lb), f"{plan}"
+    assert_parity(a, oracle_run(w)[0], "int8 integers")
+
+
+def test_fp8_subnormal_codes_are_not_flushed(torch, lib):
+    # One key per sequence made of subnormal codes (exponent field 0, values m/8 * 2^-6)
+    # with a large row scale, so its score dominates only if the subnormals survive the
+    # conversion; the values of that token are subnormal codes too.
+    cfg = SMALL.with_(kv_dtype="fp8", n_q_heads=2, n_kv_heads=2, len_lo=20, len_hi=40)
+    w = generate(cfg, seed=18)
+    w.q = np.abs(w.q)
+    rng = np.random.default_rng(18)
+    for b in range(cfg.batch):
+        page = w.block_table[b, 0]
+        w.k_pages[page, :, 3, :] = rng.integers(1, 8, size=(2, 128))      # +m/8 * 2^-6
+        w.v_pages[page, :, 3, :] = rng.integers(1, 8, size=(2, 128)) | 0x80
+        w.k_scale[page, :, 3] = 400.0
+        w.v_scale[page, :, 3] = 64.0
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w)
+    assert_parity(got, ref, "fp8 subnormals")
+    assert_lse(lse, ref_lse, "lse")
+    assert np.all(ref < 0), "the subnormal token must dominate the reference"
+
+
 def test_output_guard_words_untouched(torch, lib):
     w = generate(SMALL, seed=15)
     d = to_dev(torch, w)
@@ -334,7 +390,7 @@ def test_one_hip_runtime_and_native_library(torch, lib):
 
 # ------------------------------------------------------------------ the preset workloads
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5, 6, 7])
 def test_preset_workload_full_size(torch, lib, index):
     """Each preset at its full size, in the launch configuration the benchmark times
     (library-chosen grid), compared elementwise on every output."""
