@@ -38,22 +38,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources that decide what the attention kernels do (kernels, their
-    internal interface and the host planner)."""
+ATTN_SOURCES = ("api.cpp", "kernels.h", "kernels.hip")
+APPEND_SOURCES = ("api.cpp", "kernels.h", "append.hip")
+
+
+def kernel_source_hash(sources=ATTN_SOURCES) -> str:
+    """Hash of the sources that decide what a kernel does (the kernel file, the internal
+    interface and the host side that plans and launches it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_phase_attention_paged_amd", "csrc")
-    for name in ("api.cpp", "kernels.h", "kernels.hip"):
+    for name in sources:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str):
+def read_traffic(workload_name: str, prefix: str = "decode_attn", sources=ATTN_SOURCES):
     """HBM bytes per launch of the dominant kernel, from the committed rocprofv3 summary
     (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter reads for a
     plain copy of known size), or None when there is none or the kernels changed since."""
-    path = os.path.join(PROFILES, f"decode_attn_{workload_name}.txt")
+    path = os.path.join(PROFILES, f"{prefix}_{workload_name}.txt")
     if not os.path.exists(path):
         return None, "no counter summary"
     fields = {}
@@ -62,7 +66,7 @@ def read_traffic(workload_name: str):
             if ":" in line and not line.startswith((" ", "#")):
                 k, v = line.split(":", 1)
                 fields.setdefault(k.strip(), v.strip())
-    if fields.get("kernel_source_sha256") != kernel_source_hash():
+    if fields.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None, "kernel changed since the counters were taken"
     try:
         return float(fields["traffic_bytes_per_launch"]), path
@@ -74,7 +78,7 @@ def cpu_baseline(w, budget_s: float = 10.0):
     """The fp64 oracle as it stands, timed on the host over a bounded sample."""
     import numpy as np
     import oracle
-    from decode_phase_attention_paged_amd.workload import kv_read_bytes
+    from decode_phase_attention_paged_amd.workload import ELEM_BYTES, SCALE_BYTES, kv_read_bytes
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -91,9 +95,8 @@ def cpu_baseline(w, budget_s: float = 10.0):
     if per_token * total_tokens > budget_s:
         cum = np.cumsum(w.seq_lens.astype(np.int64))
         n = max(1, int(np.searchsorted(cum, budget_s / per_token)))
-    elem = 1 if c.kv_dtype == "int8" else 2
-    sample_bytes = kv_read_bytes(w.seq_lens[:n], c.n_kv_heads, c.head_dim, elem,
-                                 4 if c.kv_dtype == "int8" else 0)
+    sample_bytes = kv_read_bytes(w.seq_lens[:n], c.n_kv_heads, c.head_dim,
+                                 ELEM_BYTES[c.kv_dtype], SCALE_BYTES[c.kv_dtype])
     reps, spent = 0, 0.0
     while reps < 1 or (spent < budget_s and reps < 50):
         t0 = time.perf_counter()
@@ -120,6 +123,23 @@ def copy_calibration(torch, nbytes: int = 1 << 30, reps: int = 3):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+# Arithmetic type named in the JSON line, by KV storage format (the kernels accumulate in fp32
+# whatever the storage type).
+DTYPE_NAMES = {"fp16": "f16", "bf16": "bf16", "int8": "i8", "fp8": "fp8e4m3"}
+
+
+def device_tensor(torch, np, a, dev):
+    """A host array on the GPU; bf16 bit patterns (uint16) become bfloat16 tensors and E4M3
+    codes (uint8) float8_e4m3fn tensors."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    t = torch.from_numpy(a).to(dev)
+    return t.view(torch.float8_e4m3fn) if a.dtype == np.uint8 else t
+
+
 # Kernels one step launches, by plan mode (stream, split, segment).
 KERNELS = {0: "stream_kernel + piece_merge_kernel", 1: "split_kernel + split_merge_kernel",
            2: "seg_kernel"}
@@ -130,7 +150,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--workgroups", type=int, default=0,
                     help="stream mode on this many workgroups, or the grid of segment mode "
                          "with --splits 1 (0 = the library's plan)")
@@ -140,6 +160,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--op", choices=["attn", "append"], default="attn",
+                    help="attn: the decode-attention step (default); append: the K/V append "
+                         "that precedes it in a decode step, on the same workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -160,11 +183,13 @@ def main():
 
     lib = binding.load_library()
     cfg = CONFIGS[args.config]
+    if args.op == "append":
+        return bench_append(args, cfg, lib, torch, np, binding, generate)
     log(f"generating {cfg.name} ...")
     w = generate(cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    t = lambda a: device_tensor(torch, np, a, dev)
     q, bt, sl = t(w.q), t(w.block_table), t(w.seq_lens)
     pool_bytes = 2 * w.k_pages.nbytes + (2 * w.k_scale.nbytes if w.k_scale is not None else 0)
     reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
@@ -174,7 +199,7 @@ def main():
         pools.append((t(w.k_pages), t(w.v_pages), t(w.k_scale), t(w.v_scale)))
     out = torch.empty(w.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    kv_type = binding.KV_INT8 if cfg.kv_dtype == "int8" else binding.KV_FP16
+    kv_type = binding._KV_CODES[cfg.kv_dtype]
     num_cus = torch.cuda.get_device_properties(dev).multi_processor_count
     plan = binding.plan(cfg.batch, cfg.max_blocks_per_seq, cfg.n_q_heads, cfg.n_kv_heads,
                         cfg.block_size, cfg.kv_dtype, args.workgroups, args.splits, num_cus)
@@ -257,7 +282,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if cfg.kv_dtype == "fp16" else "i8",
+        "dtype": DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
@@ -280,6 +305,149 @@ def main():
             "kernel": KERNELS[plan.mode] + " (one step)",
             "avg_launch_us": round(avg_launch_s * 1e6, 3),
         },
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(record), flush=True)
+
+
+def append_bytes(batch: int, n_kv_heads: int, head_dim: int, kv_dtype: str) -> int:
+    """Algorithmic bytes of one append launch that writes every row: the new K and V rows
+    read (16-bit), the stored rows written (16-bit, or 8-bit codes plus an fp32 row scale),
+    and each sequence's position and block-table entry read."""
+    rows = batch * n_kv_heads
+    written = head_dim * 2 if kv_dtype in ("fp16", "bf16") else head_dim + 4
+    return rows * 2 * (head_dim * 2 + written) + batch * 8
+
+
+def append_cpu_baseline(w, table, positions, new, budget_s: float = 10.0):
+    """oracle.append_kv as it stands, timed on the host over whole launches."""
+    import oracle
+    c = w.config
+    reps, spent = 0, 0.0
+    while reps < 1 or (spent < budget_s and reps < 200):
+        t0 = time.perf_counter()
+        oracle.append_kv(w.k_pages, w.v_pages, table, positions, new[0], new[1], c.block_size,
+                         w.k_scale, w.v_scale)
+        spent += time.perf_counter() - t0
+        reps += 1
+    nbytes = append_bytes(c.batch, c.n_kv_heads, c.head_dim, c.kv_dtype)
+    return {"value": round(nbytes * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} whole launches ({c.batch * c.n_kv_heads} rows each) in "
+                      f"{spent:.1f} s, pool copies included"}
+
+
+def bench_append(args, cfg, lib, torch, np, binding, generate):
+    """Time decode_attn_append: every sequence of the workload writes its next token
+    (position L_b) into its page slot; sequences whose next token starts a new page get a
+    fresh page. The new rows are fp16 ~ N(0, 1) scaled per row by U(0.1, 10)."""
+    log(f"generating {cfg.name} for the append ...")
+    w = generate(cfg)
+    table = w.block_table.copy()
+    positions = w.seq_lens.astype(np.int32).copy()
+    fresh = 0
+    for b in range(cfg.batch):
+        j = int(positions[b]) // cfg.block_size
+        if j >= table.shape[1]:
+            positions[b] = int(positions[b]) - 1      # a full table: rewrite the last slot
+        elif table[b, j] < 0:
+            table[b, j] = w.num_pages + fresh
+            fresh += 1
+    n_pages = w.num_pages + fresh
+    rng = np.random.default_rng(w.seed + 1)
+    shape = (cfg.batch, cfg.n_kv_heads, cfg.head_dim)
+    new = [(rng.standard_normal(shape, dtype=np.float32) *
+            rng.uniform(0.1, 10, size=shape[:2] + (1,))).astype(np.float32) for _ in range(2)]
+    new = [(x.view(np.uint32) >> 16).astype(np.uint16) if cfg.kv_dtype == "bf16"
+           else x.astype(np.float16) for x in new]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    scaled = cfg.kv_dtype in ("int8", "fp8")
+    pool_shape = (n_pages, cfg.n_kv_heads, cfg.block_size, cfg.head_dim)
+    elem = {"fp16": torch.float16, "bf16": torch.bfloat16, "int8": torch.int8,
+            "fp8": torch.float8_e4m3fn}[cfg.kv_dtype]
+    pool_bytes = 2 * n_pages * cfg.n_kv_heads * cfg.block_size * (
+        cfg.head_dim * (1 if scaled else 2) + (4 if scaled else 0))
+    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    t = lambda a: device_tensor(torch, np, a, dev)
+    bt, pos = t(table), t(positions)
+    sets = []
+    for _ in range(reps):
+        kp = torch.zeros(pool_shape, dtype=torch.uint8 if scaled else torch.int16,
+                         device=dev).view(elem)
+        vp = torch.zeros_like(kp)
+        ks = torch.zeros(pool_shape[:3], dtype=torch.float32, device=dev) if scaled else None
+        vs = torch.zeros(pool_shape[:3], dtype=torch.float32, device=dev) if scaled else None
+        sets.append((t(new[0]), t(new[1]), kp, vp, ks, vs))
+    stream = torch.cuda.current_stream(dev)
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    kv_type = binding._KV_CODES[cfg.kv_dtype]
+    call_args = [(p(kn), p(vn), p(bt), p(pos), cfg.batch, cfg.max_blocks_per_seq, n_pages,
+                  cfg.n_kv_heads, cfg.head_dim, cfg.block_size, kv_type, p(kp), p(vp), p(ks),
+                  p(vs), s_handle) for kn, vn, kp, vp, ks, vs in sets]
+
+    def step(i):
+        st = lib.decode_attn_append(*call_args[i % reps])
+        if st != 0:
+            raise RuntimeError(f"decode_attn_append failed: {binding.STATUS.get(st, st)}")
+
+    nbytes = append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.kv_dtype)
+    log(f"append: rows={cfg.batch * cfg.n_kv_heads} fresh_pages={fresh} replicas={reps} "
+        f"bytes/launch={nbytes}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    stop_ev.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start_ev.elapsed_time(stop_ev)
+    ms_per_step = total_ms / args.steps
+    gbs = nbytes * args.steps / (total_ms / 1e3) / 1e9
+    log(f"steps={args.steps} total={total_ms:.3f} ms us/step={ms_per_step * 1e3:.2f} "
+        f"GB/s={gbs:.1f}")
+    traffic, traffic_src = read_traffic(cfg.name, prefix="decode_attn_append",
+                                       sources=APPEND_SOURCES)
+    log(f"traffic: {traffic} ({traffic_src})")
+    baseline = None
+    if not args.no_cpu_baseline:
+        w_host = w
+        if fresh:
+            grow = lambda a, fill: None if a is None else np.concatenate(
+                [a, np.full((fresh,) + a.shape[1:], fill, dtype=a.dtype)])
+            w_host = type(w)(**{**w.__dict__, "k_pages": grow(w.k_pages, 0),
+                                "v_pages": grow(w.v_pages, 0), "k_scale": grow(w.k_scale, 0),
+                                "v_scale": grow(w.v_scale, 0)})
+        baseline = append_cpu_baseline(w_host, table, positions, new)
+        log(f"cpu baseline: {baseline}")
+    record = {
+        "metric": "decode K/V append GB/s (fraction of MI355X HBM peak) + µs/launch",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp16": "f16", "bf16": "bf16", "int8": "f16->i8",
+                  "fp8": "f16->fp8e4m3"}[cfg.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "_append", "batch": cfg.batch,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
+                   "rows": cfg.batch * cfg.n_kv_heads, "fresh_pages": fresh, "replicas": reps,
+                   "bytes_per_launch": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "append_kernel", "avg_launch_us": round(ms_per_step * 1e3, 3)},
         "cpu_baseline": baseline,
     }
     print(json.dumps(record), flush=True)
