@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="capture this many consecutive steps in one HIP graph and time "
+                         "replays of it (the step count is rounded up to a multiple)")
     ap.add_argument("--op", choices=["attn", "append"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
                          "that precedes it in a decode step, on the same workload")
@@ -235,6 +238,27 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph > 0:
+        # The same calls, recorded on a capture stream, args.graph steps per graph; replays
+        # run on torch's current stream, where the events below are recorded.
+        cap = torch.cuda.Stream()
+        handle = ctypes.c_void_p(cap.cuda_stream)
+        captured = [(kind, a[:-1] + (handle,)) for kind, a in call_args]
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.graph):
+                kind, a = captured[i % reps]
+                st = lib.decode_attn(*a) if kind == "auto" else lib.decode_attn_ex(*a)
+                if st != 0:
+                    raise RuntimeError(f"decode_attn failed in capture: {binding.STATUS.get(st, st)}")
+        torch.cuda.synchronize()
+        args.steps = -(-args.steps // args.graph) * args.graph
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"graph: {args.graph} steps per replay, {args.steps // args.graph} replays timed")
+
     # Timed region: exactly K back-to-back steps between one pair of HIP events recorded
     # on the launch stream. No event sits between steps: an event record between two
     # launches delays the second one by several microseconds on this GPU.
@@ -243,8 +267,12 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start_ev.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
+    if graph is not None:
+        for _ in range(args.steps // args.graph):
+            graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
     stop_ev.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -293,6 +321,7 @@ def main():
             "plan": {"mode": binding._MODE_NAMES[plan.mode],
                      "workgroups": plan.num_workgroups, "splits": plan.num_splits},
             "replicas": reps,
+            "graph_steps": args.graph,
             "kv_bytes_per_step": int(w.kv_bytes),
         },
         "roofline": {

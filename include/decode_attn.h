@@ -131,7 +131,8 @@ typedef struct {
  * The plan is the library's choice for the current device (decode_attn_plan with no
  * request), and the library uses a workspace it owns: one buffer per device, grown with
  * hipMalloc on demand and kept until the process ends. This entry point therefore may
- * allocate (on its first call for a shape), and two calls that overlap on one device
+ * allocate (on its first call for a shape; capture it in a HIP graph only after such a
+ * call), and two calls that overlap on one device
  * (different streams or host threads) must not share that workspace; such callers use
  * decode_attn_ex. Returns a decode_attn_status.
  */
@@ -173,7 +174,9 @@ int decode_attn_plan(int batch, int max_blocks_per_seq, int n_q_heads, int n_kv_
  * plan's workspace_bytes, 256-byte aligned; it may be NULL when that is 0 (segment mode
  * needs none). Its contents on entry do not matter and on return are unspecified; it must
  * not be in use by another call still running. lse_out (nullable, 4-byte aligned)
- * receives lse[b, h] as defined above. Returns a decode_attn_status.
+ * receives lse[b, h] as defined above. Every launch is a kernel (no memset, copy or
+ * allocation), so the call can be captured in a HIP graph and replayed. Returns a
+ * decode_attn_status.
  */
 int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
                    const float* k_scale, const float* v_scale,
