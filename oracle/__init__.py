@@ -13,6 +13,7 @@ from .decode import (  # noqa: F401
     kv_head_of,
 )
 from .append import append_kv, quantize_row, quantize_row_fp8  # noqa: F401
+from .prefill import prefill_attention  # noqa: F401
 from .formats import (  # noqa: F401
     bf16_to_float64,
     e4m3_from_float32,
