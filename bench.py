@@ -40,6 +40,8 @@ def log(msg):
 
 ATTN_SOURCES = ("api.cpp", "kernels.h", "kernels.hip")
 APPEND_SOURCES = ("api.cpp", "kernels.h", "append.hip")
+PREFILL_SOURCES = ("api.cpp", "kernels.h", "prefill.hip")
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
 
 
 def kernel_source_hash(sources=ATTN_SOURCES) -> str:
@@ -150,7 +152,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8],
+                    help="workload preset (0 = the op's default: 2 for attn and append, "
+                         "8 for prefill)")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="stream mode on this many workgroups, or the grid of segment mode "
                          "with --splits 1 (0 = the library's plan)")
@@ -163,9 +167,10 @@ def main():
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many consecutive steps in one HIP graph and time "
                          "replays of it (the step count is rounded up to a multiple)")
-    ap.add_argument("--op", choices=["attn", "append"], default="attn",
+    ap.add_argument("--op", choices=["attn", "append", "prefill"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
-                         "that precedes it in a decode step, on the same workload")
+                         "that precedes it in a decode step, on the same workload; prefill: "
+                         "chunked-prefill attention (default workload: the prefill preset)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -185,9 +190,13 @@ def main():
         return
 
     lib = binding.load_library()
+    if args.config == 0:
+        args.config = 8 if args.op == "prefill" else 2
     cfg = CONFIGS[args.config]
     if args.op == "append":
         return bench_append(args, cfg, lib, torch, np, binding, generate)
+    if args.op == "prefill":
+        return bench_prefill(args, cfg, lib, torch, np, binding, generate)
     log(f"generating {cfg.name} ...")
     w = generate(cfg)
     dev = torch.device("cuda:0")
@@ -477,6 +486,116 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "append_kernel", "avg_launch_us": round(ms_per_step * 1e3, 3)},
+        "cpu_baseline": baseline,
+    }
+    print(json.dumps(record), flush=True)
+
+
+def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
+    """oracle.prefill_attention as it stands, timed on the host over whole sequences."""
+    import numpy as np
+    import oracle
+    from decode_phase_attention_paged_amd.workload import prefill_flops
+    c = w.config
+    done_flops, spent, seqs = 0, 0.0, 0
+    order = np.argsort(w.seq_lens)
+    for b in order:
+        rows = slice(int(q_start[b]), int(q_start[b + 1]))
+        sub = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
+                                 w.seq_lens[b:b + 1], sub, w.scale)
+        spent += time.perf_counter() - t0
+        done_flops += prefill_flops(w.seq_lens[b:b + 1], sub, c.n_q_heads, c.head_dim)
+        seqs += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{seqs} of {c.batch} sequences, shortest first ({spent:.1f} s)"}
+
+
+def bench_prefill(args, cfg, lib, torch, np, binding, generate):
+    """Time decode_attn_prefill: every sequence's last C_b = min(chunk, L_b) tokens attend
+    causally over its cache, all sequences in one launch. Throughput counts the algorithmic
+    flops (4 D per visible token per row and query head)."""
+    from decode_phase_attention_paged_amd.workload import prefill_flops, prefill_rows
+    if cfg.chunk <= 0:
+        raise SystemExit(f"preset {cfg.name} has no chunk size; use a prefill preset")
+    log(f"generating {cfg.name} ...")
+    w = generate(cfg)
+    q_host, qs_host = prefill_rows(w)
+    flops = prefill_flops(w.seq_lens, qs_host, cfg.n_q_heads, cfg.head_dim)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = lambda a: device_tensor(torch, np, a, dev)
+    q, qs, bt, sl = t(q_host), t(qs_host), t(w.block_table), t(w.seq_lens)
+    pool_bytes = 2 * w.k_pages.nbytes
+    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    pools = [(t(w.k_pages), t(w.v_pages)) for _ in range(reps)]
+    out = torch.empty(q_host.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda x: ctypes.c_void_p(x.data_ptr())
+    total = q_host.shape[0]
+    call_args = [(p(q), p(qs), p(kp), p(vp), p(bt), p(sl), cfg.batch, total,
+                  cfg.max_blocks_per_seq, w.num_pages, cfg.n_q_heads, cfg.n_kv_heads,
+                  cfg.head_dim, cfg.block_size, binding.KV_FP16, cfg.chunk, float(w.scale),
+                  p(out), s_handle) for kp, vp in pools]
+
+    def step(i):
+        st = lib.decode_attn_prefill(*call_args[i % reps])
+        if st != 0:
+            raise RuntimeError(f"decode_attn_prefill failed: {binding.STATUS.get(st, st)}")
+
+    log(f"prefill: rows={total} chunk={cfg.chunk} replicas={reps} flops/step={flops / 1e9:.1f} G")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    stop_ev.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start_ev.elapsed_time(stop_ev)
+    ms_per_step = total_ms / args.steps
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    log(f"steps={args.steps} total={total_ms:.3f} ms us/step={ms_per_step * 1e3:.2f} "
+        f"TFLOP/s={tflops:.1f} ({tflops / MFMA_F16_PEAK_TFLOPS:.3f} of peak)")
+    traffic, traffic_src = read_traffic(cfg.name, prefix="decode_attn_prefill",
+                                        sources=PREFILL_SOURCES)
+    log(f"traffic: {traffic} ({traffic_src})")
+    baseline = None
+    if not args.no_cpu_baseline:
+        baseline = prefill_cpu_baseline(w, q_host, qs_host)
+        log(f"cpu baseline: {baseline}")
+    record = {
+        "metric": "chunked-prefill attention TFLOP/s (fraction of MI355X fp16 matrix peak)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "chunk": cfg.chunk, "rows": total,
+                   "seq_lens": f"uniform [{cfg.len_lo}, {cfg.len_hi}], seed {w.seed}",
+                   "flops_per_step": int(flops), "kv_bytes_per_step": int(w.kv_bytes),
+                   "replicas": reps},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "prefill_kernel", "avg_launch_us": round(ms_per_step * 1e3, 3)},
         "cpu_baseline": baseline,
     }
     print(json.dumps(record), flush=True)

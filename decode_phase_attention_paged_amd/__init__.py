@@ -8,11 +8,12 @@ The binding is imported lazily so that the workload generator can be used on
 a machine where the library has not been built.
 """
 
-__all__ = ["decode_attn", "decode_attn_ex", "decode_attn_append", "plan", "binding", "workload"]
+__all__ = ["decode_attn", "decode_attn_ex", "decode_attn_append", "decode_attn_prefill", "plan",
+           "binding", "workload"]
 
 
 def __getattr__(name):
-    if name in ("decode_attn", "decode_attn_ex", "decode_attn_append", "plan"):
+    if name in ("decode_attn", "decode_attn_ex", "decode_attn_append", "decode_attn_prefill", "plan"):
         from . import binding
         return getattr(binding, name)
     if name in ("binding", "workload"):

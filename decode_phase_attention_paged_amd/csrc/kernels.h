@@ -107,4 +107,23 @@ struct AppendArgs {
 };
 hipError_t launch_append(KvType kv, const AppendArgs& a, hipStream_t stream);
 
+// Chunked-prefill attention over the paged cache (prefill.hip); fp16 K/V.
+struct PrefillArgs {
+  const void* q;               // fp16 [T, Hq, D]: every sequence's chunk rows, stacked
+  const int32_t* q_start;      // int32 [B + 1]: sequence b's rows are q_start[b] .. q_start[b+1]-1
+  const void* k_pages;         // fp16 [NP, Hkv, bs, D]
+  const void* v_pages;
+  const int32_t* block_table;  // int32 [B, MB]
+  const int32_t* seq_lens;     // int32 [B]: L_b, counting the chunk
+  float* out;                  // fp32 [T, Hq, D]
+  int batch;
+  int total_rows;              // T
+  int max_blocks;              // MB
+  int num_pages;               // NP
+  int n_kv_heads;
+  float scale_log2;            // softmax scale * log2(e)
+};
+// max_chunk bounds C_b for sizing the grid only; longer chunks are still covered.
+hipError_t launch_prefill(int group, const PrefillArgs& a, int max_chunk, hipStream_t stream);
+
 }  // namespace dattn

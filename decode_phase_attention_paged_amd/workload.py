@@ -40,6 +40,8 @@ __all__ = [
     "generate",
     "kv_read_bytes",
     "other_bytes",
+    "prefill_rows",
+    "prefill_flops",
 ]
 
 
@@ -59,6 +61,7 @@ class Config:
     peaky_fraction: float = 0.0  # fraction of each (sequence, KV head)'s keys scaled
     peaky_factor: float = 1.0
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
+    chunk: int = 0              # prefill presets: new tokens per sequence (C_b = min(chunk, L_b))
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -82,6 +85,7 @@ CONFIGS = {
     5: Config(5, "int8_mha_b200", 200, 32, 32, 128, 16, 18, 530, "int8"),
     6: Config(6, "llama2_7b_mha_b48_bf16", 48, 32, 32, 128, 16, 18, 563, "bf16"),
     7: Config(7, "fp8_mha_b200", 200, 32, 32, 128, 16, 18, 530, "fp8"),
+    8: Config(8, "llama3_8b_gqa_prefill_c512", 8, 32, 8, 128, 16, 512, 4096, "fp16", chunk=512),
 }
 
 # Storage bytes per element and per row scale, by kv_dtype.
@@ -161,6 +165,32 @@ def _poison_unused_slots(w: Workload, n_used_pages: int) -> None:
         else:
             w.k_scale[unused] = np.float32(np.nan)
             w.v_scale[unused] = np.float32(np.nan)
+
+
+def prefill_rows(w: "Workload", chunk: Optional[int] = None, seed: Optional[int] = None):
+    """Chunk query rows for a prefill step over workload w: C_b = min(chunk, L_b) rows per
+    sequence, stacked in sequence order. Returns (q [T, Hq, D] fp16 ~ N(0, 1), q_start
+    int32 [B + 1]). Drawn from their own stream (seed + 1), so w's draws are unchanged."""
+    c = w.config
+    chunk = c.chunk if chunk is None else int(chunk)
+    sizes = np.minimum(np.asarray(w.seq_lens, dtype=np.int64), chunk)
+    q_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng((w.seed if seed is None else int(seed)) + 1)
+    q = rng.standard_normal((int(q_start[-1]), c.n_q_heads, c.head_dim),
+                            dtype=np.float32).astype(np.float16)
+    return q, q_start
+
+
+def prefill_flops(seq_lens, q_start, n_q_heads: int, head_dim: int) -> int:
+    """Algorithmic flops of a prefill step: for every chunk row and query head, 2 D flops
+    per visible token for q . k and 2 D for the weighted sum of V; row i of a chunk of C_b
+    sees L_b - C_b + i + 1 tokens."""
+    total = 0
+    for b in range(len(seq_lens)):
+        n = int(seq_lens[b])
+        c = int(q_start[b + 1] - q_start[b])
+        total += c * (n - c) + c * (c + 1) // 2
+    return total * n_q_heads * 4 * head_dim
 
 
 def _bf16_bits(x32: np.ndarray) -> np.ndarray:

@@ -224,10 +224,50 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
                        int kv_dtype, void* k_pages, void* v_pages, float* k_scale,
                        float* v_scale, hipStream_t stream);
 
+/*
+ * Chunked-prefill attention over the paged cache: several new tokens per sequence at once.
+ * The prefill phase runs a prompt's tokens through the model and fills the cache (page
+ * "Eine LLM-Inferenz-Engine von Grund auf mit C++ und CUDA bauen", section 1.1; handling
+ * several prompt tokens together with FlashAttention-style fused attention is among its
+ * next steps, section 4), and swiftLLM's feature list piggybacks prefill chunks on decode
+ * batches. Sequence b's chunk is its last C_b = q_start[b+1] - q_start[b] tokens, whose K
+ * and V rows are already in the cache (L_b = seq_lens[b] counts them); chunk row i sits at
+ * position p = L_b - C_b + i and attends causally to tokens 0 .. p:
+ *
+ *     out[q_start[b] + i, h, :] = sum_{t <= p} softmax_t(scale * <q[.., h, :], K_b[g,t,:]>) V_b[g,t,:]
+ *
+ * with g = h / G. A decode token is a chunk of one, so prefill chunks and decode tokens can
+ * share a call.
+ *
+ *     q         fp16 [total_rows, n_q_heads, head_dim], 16-byte aligned: all chunks' rows
+ *     q_start   int32 [batch + 1]: 0 <= q_start[b] <= q_start[b+1] <= total_rows
+ *     k_pages, v_pages, block_table, seq_lens, num_pages: as for decode_attn (fp16 pools)
+ *     max_chunk an upper bound on C_b, used only to size the grid (total_rows is always
+ *               safe); longer chunks are still computed in full
+ *     out       fp32 [total_rows, n_q_heads, head_dim], 16-byte aligned; rows outside every
+ *               chunk are not written
+ *
+ * Both products run on the matrix cores (fp16 inputs, fp32 accumulation), with the softmax
+ * weights rounded to fp16 for the second one. Bad device values never fault: a sequence
+ * whose q_start range leaves [0, total_rows] or is empty is skipped; one whose chunk is
+ * longer than L_b, whose L_b exceeds the table, or whose table holds a page id outside
+ * [0, num_pages) among its first ceil(L_b / block_size) entries gets NaN in all its rows.
+ * Supported: kv_dtype FP16 (others return DECODE_ATTN_ERR_UNSUPPORTED), head_dim 128,
+ * block_size 16, G in {1, 2, 4, 8}, batch and n_kv_heads up to 65535. Asynchronous on
+ * `stream`; never allocates; capturable in a HIP graph. Returns a decode_attn_status.
+ */
+int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pages,
+                        const void* v_pages, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int total_rows,
+                        int max_blocks_per_seq, int num_pages, int n_q_heads, int n_kv_heads,
+                        int head_dim, int block_size, int kv_dtype, int max_chunk, float scale,
+                        float* out, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);
 
-/* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats. */
+/* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats;
+   6.1 adds decode_attn_prefill. */
 int decode_attn_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_plan",
-        "decode_attn_status_string", "decode_attn_version"])
+        "decode_attn_prefill", "decode_attn_status_string", "decode_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,7 +51,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 6
+    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 1
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -267,3 +267,41 @@ def call_append(lib, **over):
 ])
 def test_append_host_validation(lib, over, status):
     assert call_append(lib, **over) == status
+
+
+# decode_attn_prefill: fake device addresses; every case fails host-side validation (or
+# enqueues nothing).
+PREFILL = dict(q=A, qs=2 * A, k=3 * A, v=4 * A, bt=5 * A, sl=6 * A, batch=2, total=10, mb=8,
+               np_=16, hq=8, hkv=2, d=128, bs=16, kv=0, chunk=8, scale=0.088, out=7 * A)
+
+
+def call_prefill(lib, **over):
+    a = dict(PREFILL, **over)
+    return lib.decode_attn_prefill(a["q"], a["qs"], a["k"], a["v"], a["bt"], a["sl"], a["batch"],
+                                   a["total"], a["mb"], a["np_"], a["hq"], a["hkv"], a["d"],
+                                   a["bs"], a["kv"], a["chunk"], a["scale"], a["out"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hq=6, hkv=4), 1),                  # Hq % Hkv != 0
+    (dict(hq=6, hkv=2), 2),                  # G = 3
+    (dict(kv=1), 2),                         # int8 pools: not supported by the prefill
+    (dict(kv=2), 2),                         # bf16
+    (dict(kv=3), 2),                         # fp8
+    (dict(kv=7), 1),                         # unknown storage type
+    (dict(d=64), 2),
+    (dict(bs=8), 2),
+    (dict(chunk=0), 1),
+    (dict(total=-1), 1),
+    (dict(qs=None), 1),
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(q=A + 8), 1),                      # q not 16-byte aligned
+    (dict(out=7 * A + 4), 1),
+    (dict(batch=70000), 2),                  # beyond the grid's z range
+    (dict(batch=-1), 1),
+    (dict(batch=0, q=None, qs=None, k=None, v=None, bt=None, sl=None, out=None), 0),
+    (dict(total=0, q=None, out=None, batch=0), 0),
+])
+def test_prefill_host_validation(lib, over, status):
+    assert call_prefill(lib, **over) == status

@@ -1,0 +1,138 @@
+"""GPU parity of decode_attn_prefill (chunked-prefill attention on the matrix cores) against
+the fp64 oracle: every chunk row within |gpu - oracle| <= 2e-3 + 1e-2 |oracle|. Chunks of
+every size class (whole prompts, single decode tokens, page-crossing, more rows than one
+workgroup block), every group size, a grid smaller than the chunks, NaN canaries in every
+slot no token owns, bad device values, and the full-size preset on sampled sequences.
+Every call goes through the C ABI."""
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_phase_attention_paged_amd.workload import CONFIGS, Config, generate, prefill_rows
+
+from test_gpu_parity import assert_parity, dev_tensor
+
+pytestmark = pytest.mark.gpu
+
+SMALL = Config(0, "small_prefill", batch=5, n_q_heads=8, n_kv_heads=2, head_dim=128,
+               block_size=16, len_lo=1, len_hi=200, kv_dtype="fp16")
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need an MI355X"
+    return t
+
+
+@pytest.fixture(scope="module")
+def lib(torch):
+    from decode_phase_attention_paged_amd import binding
+    return binding
+
+
+def chunk_layout(lens, rng, kinds=("full", "one", "rand")):
+    sizes = []
+    for i, n in enumerate(lens):
+        kind = kinds[i % len(kinds)]
+        n = int(n)
+        sizes.append(n if kind == "full" else 1 if kind == "one" else int(rng.integers(1, n + 1)))
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+def run(torch, lib, w, q, q_start, max_chunk=None, out=None):
+    t = lambda a: dev_tensor(torch, a)
+    got = lib.decode_attn_prefill(t(q), t(q_start), t(w.k_pages), t(w.v_pages), t(w.block_table),
+                                  t(w.seq_lens), w.scale, max_chunk=max_chunk, out=out)
+    torch.cuda.synchronize()
+    return got.cpu().numpy()
+
+
+def reference(w, q, q_start):
+    return oracle.prefill_attention(q, w.k_pages, w.v_pages, w.block_table, w.seq_lens,
+                                    q_start, w.scale)[0]
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_small_mixed_chunks(torch, lib, group, seed):
+    cfg = SMALL.with_(n_q_heads=2 * group, n_kv_heads=2)
+    w = generate(cfg, seed=200 + seed, poison=True, extra_pages=3)
+    rng = np.random.default_rng(seed)
+    q_start = chunk_layout(w.seq_lens, rng)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print(f"case prefill G={group} seed={seed} lens={w.seq_lens.tolist()} "
+          f"chunks={np.diff(q_start).tolist()}", flush=True)
+    got = run(torch, lib, w, q, q_start)
+    assert np.isfinite(got).all(), "a NaN canary leaked"
+    assert_parity(got, reference(w, q, q_start), f"prefill G={group}")
+
+
+@pytest.mark.parametrize("max_chunk", [1, 7, 64, 10000])
+def test_grid_smaller_than_the_chunks(torch, lib, max_chunk):
+    # The grid is sized from max_chunk; workgroups loop over the remaining row blocks.
+    cfg = SMALL.with_(batch=3, len_lo=150, len_hi=300)
+    w = generate(cfg, seed=210)
+    rng = np.random.default_rng(210)
+    q_start = chunk_layout(w.seq_lens, rng, kinds=("full",))
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print(f"case prefill max_chunk={max_chunk}", flush=True)
+    got = run(torch, lib, w, q, q_start, max_chunk=max_chunk)
+    assert_parity(got, reference(w, q, q_start), f"max_chunk {max_chunk}")
+
+
+def test_one_token_chunks_match_decode(torch, lib):
+    # A batch of one-token chunks is a decode step: same results as decode_attn within the
+    # tolerance (the two kernels round differently).
+    w = generate(SMALL, seed=211)
+    q_start = np.arange(SMALL.batch + 1, dtype=np.int32)
+    got = run(torch, lib, w, w.q, q_start)
+    t = lambda a: dev_tensor(torch, a)
+    dec = lib.decode_attn(t(w.q), t(w.k_pages), t(w.v_pages), t(w.block_table), t(w.seq_lens),
+                          w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(w.q, w.k_pages, w.v_pages, w.block_table, w.seq_lens, w.scale)[0]
+    assert_parity(got, ref, "one-token chunks")
+    assert_parity(dec.cpu().numpy(), ref, "decode")
+
+
+def test_bad_values_give_nan_and_leave_other_rows(torch, lib):
+    cfg = SMALL.with_(batch=4, len_lo=40, len_hi=90)
+    w = generate(cfg, seed=212)
+    rng = np.random.default_rng(212)
+    q_start = chunk_layout(w.seq_lens, rng, kinds=("rand",))
+    q = rng.standard_normal((int(q_start[-1]) + 5, cfg.n_q_heads, 128)).astype(np.float16)
+    table = w.block_table.copy()
+    table[1, 1] = w.num_pages + 7                   # a bad page id for sequence 1
+    lens = w.seq_lens.copy()
+    lens[2] = int(q_start[3] - q_start[2]) - 1       # sequence 2: chunk longer than L_b
+    t = lambda a: dev_tensor(torch, a)
+    out = torch.full(q.shape, 777.0, dtype=torch.float32, device="cuda:0")
+    lib.decode_attn_prefill(t(q), t(q_start), t(w.k_pages), t(w.v_pages), t(table), t(lens),
+                            w.scale, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isnan(got[q_start[1]:q_start[2]]).all()
+    assert np.isnan(got[q_start[2]:q_start[3]]).all()
+    assert np.all(got[q_start[-1]:] == 777.0), "rows outside every chunk were written"
+    keep = np.r_[q_start[0]:q_start[1], q_start[3]:q_start[4]]
+    ref = reference(w, q[:q_start[-1]], q_start)
+    assert_parity(got[keep], ref[keep], "good sequences")
+
+
+def test_full_size_preset_on_sampled_sequences(torch, lib):
+    """The prefill preset at full size, in the launch the benchmark times; the oracle
+    checks two whole sequences (the shortest and the longest) and every row's finiteness."""
+    cfg = CONFIGS[8]
+    w = generate(cfg)
+    q, q_start = prefill_rows(w)
+    print(f"case prefill preset rows={q.shape[0]}", flush=True)
+    got = run(torch, lib, w, q, q_start, max_chunk=cfg.chunk)
+    assert np.isfinite(got).all()
+    for b in (int(np.argmin(w.seq_lens)), int(np.argmax(w.seq_lens))):
+        rows = slice(int(q_start[b]), int(q_start[b + 1]))
+        sub_start = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
+        ref = oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
+                                       w.seq_lens[b:b + 1], sub_start, w.scale)[0]
+        assert_parity(got[rows], ref, f"preset sequence {b}")
