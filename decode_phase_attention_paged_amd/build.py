@@ -13,6 +13,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -34,32 +35,60 @@ def hipcc() -> str:
     return path
 
 
-def compile_cmd(out: str = LIB_PATH, extra=()) -> list:
+def _common_flags(extra=()) -> list:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-mcode-object-version=5", "-Wall", "-Wno-unused-command-line-argument",
         *DEVICE_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *extra,
-        *[os.path.join(CSRC, s) for s in SOURCES], "-o", out,
     ]
 
 
+def compile_cmd(out: str = LIB_PATH, extra=()) -> list:
+    """One hipcc line that compiles and links every source (for reference and tools)."""
+    return [hipcc(), *_common_flags(extra), "-shared",
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
+def _filter_stderr(text: str) -> str:
+    # hipcc's host pass does not know the packed-fp32 feature name; that warning is
+    # expected. Anything else is shown.
+    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    return "\n".join(lines) + "\n" if any(ln.strip() for ln in lines) else ""
+
+
 def build(verbose: bool = True) -> str:
-    """Compile the library (always recompiles) and return its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = compile_cmd(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr.strip():
-        # hipcc's host pass does not know the packed-fp32 feature name; that warning is
-        # expected. Anything else is shown.
-        lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
-        if any(ln.strip() for ln in lines):
-            sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB_PATH)
+    """Compile the library (always recompiles) and return its path. The sources compile
+    to objects in parallel (one hipcc per file), then link into one shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = tempfile.mkdtemp(prefix="decode_attn_build_")
+    try:
+        def compile_one(src):
+            obj = os.path.join(objdir, src + ".o")
+            cmd = [hipcc(), *_common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            results = list(pool.map(compile_one, SOURCES))
+        for (obj, res), src in zip(results, SOURCES):
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError(f"hipcc failed on {src} with exit code {res.returncode}")
+            if verbose and res.stderr.strip():
+                sys.stderr.write(_filter_stderr(res.stderr))
+        tmp = LIB_PATH + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+               *[obj for obj, _ in results], "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
+        os.replace(tmp, LIB_PATH)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB_PATH
 
 

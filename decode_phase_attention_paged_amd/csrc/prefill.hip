@@ -8,16 +8,22 @@
 // p = L_b - C_b + i and attends to tokens 0 .. p. A decode token is a chunk of one.
 //
 // Unlike decode, this is a dense contraction: each K/V page is used by every chunk row of
-// the (sequence, KV head), G * C_b query rows, so the page tiles are staged once in LDS and
-// both products run on MFMA (v_mfma_f32_16x16x16_f16, fp32 accumulate):
-//   S^T[token][row] = K[token][:] . Q[row][:]   (A = K tile from LDS, B = Q^T in VGPRs)
-//   O[row][d]      += P[row][token] V[token][d]  (A = P as fp16, straight from S^T's layout;
-//                                                B = V tile read as columns from LDS)
-// with the online-normaliser softmax per row in between (fp32, log2 units). Rows are
-// (chunk token, query head of the group) pairs, 16 per wavefront, 64 per workgroup.
+// the (sequence, KV head), G * C_b query rows. A workgroup owns 128 rows (4 waves x 2
+// groups of 16) of one (sequence, KV head) and walks the cache in tiles of 64 tokens (four
+// pages), staged once in LDS: K as [token][d], V transposed to [d][token]. Both products run
+// on gfx950's double-rate v_mfma_f32_16x16x32_f16 (fp16 in, fp32 accumulate), transposed
+// so that each lane keeps one query row throughout:
+//   S^T[token][row] = K[token][:] . Q[row][:]      A = K tile (LDS), B = Q^T (VGPRs)
+//   O^T[d][row]    += V^T[d][token] P^T[token][row] A = V^T tile (LDS), B = P^T (VGPRs)
+// The first product leaves lane l with tokens of row l % 16, which is exactly the layout the
+// second one takes P^T in, and its result O^T keeps row l % 16 in lane l, so the online-
+// normaliser rescale (fp32, log2 units) is a per-lane multiply with no cross-lane traffic.
 //
-// 16x16x16 MFMA operand layout (lane l, k = 4 * (l / 16) + e for e = 0..3):
-//   A: A[l % 16][k];  B: B[k][l % 16];  D: D[4 * (l / 16) + e][l % 16].
+// 16x16x32 operand layout (lane l, q = l / 16, item e): A[l % 16][slot 8q + e] for e < 8,
+// B[slot 8q + e][l % 16], D[4q + e][l % 16] for e < 4. A and B share the slot order, so a
+// contraction is correct for any assignment of the 32 k values to slots, provided A and B
+// use the same one; the P V product assigns slot 8q + e to tile token 32c + 4q + e (e < 4)
+// and 32c + 16 + 4q + (e - 4) (e >= 4), which is how the first product's output falls.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,23 +35,37 @@ namespace {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kRowsPerWave = 16;
+constexpr int kRowGroups = 2;                         // 16-row groups per wave
+constexpr int kRowsPerWave = 16 * kRowGroups;
 constexpr int kRowsPerBlock = kRowsPerWave * kPfWaves;
-constexpr int kTileStride = kHeadDim * 2 + 16;   // LDS bytes per token row (padded: no bank clash)
+constexpr int kTileTok = 64;                          // tokens staged per step
+constexpr int kPagesPerTile = kTileTok / kBlockSize;
+constexpr int kKStride = kHeadDim * 2 + 16;           // LDS bytes per K token row (padded)
+constexpr int kVtStride = kTileTok * 2 + 8;           // LDS bytes per V^T d row (padded)
+constexpr int kPageBytes = kBlockSize * kHeadDim * 2; // one (page, KV head) fp16 tile
 constexpr float kNegInfPf = -__builtin_huge_valf();
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+static_assert(kPagesPerTile * kBlockSize == kTileTok, "tiles are whole pages");
+static_assert(kTileTok * kHeadDim * 2 == kPfThreads * 4 * 16, "four 16-byte K loads per thread");
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 // One workgroup: query-row block mb of (sequence b, KV head g), looping over further blocks
 // gridDim.x apart.
 template <int kGroup>
-__global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[kBlockSize * kTileStride];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[kBlockSize * kTileStride];
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[kTileTok * kKStride];
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[kHeadDim * kVtStride];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
@@ -64,138 +84,204 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillArgs a) {
   if (r0 < 0 || r1 > a.total_rows || C <= 0) return;
   const bool bad_len = C > L || L > a.max_blocks * kBlockSize;
   const int nb = bad_len ? 0 : (L + kBlockSize - 1) / kBlockSize;
+  const int32_t* table = a.block_table + static_cast<size_t>(b) * a.max_blocks;
 
   // Every page id of the sequence must be in range, else all its rows are NaN.
   if (tid == 0) s_bad = bad_len ? 1 : 0;
   __syncthreads();
   for (int j = tid; j < nb; j += kPfThreads) {
-    const int phys = a.block_table[static_cast<size_t>(b) * a.max_blocks + j];
-    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(a.num_pages)) s_bad = 1;
+    if (static_cast<unsigned>(table[j]) >= static_cast<unsigned>(a.num_pages)) s_bad = 1;
   }
   __syncthreads();
   const bool bad = s_bad != 0;
 
   const int rows_total = C * kGroup;
-  const int col = lane & 15;        // this lane's row in S^T / the B operand
-  const int quad = lane >> 4;       // which 4 of the 16 k-indices this lane holds
+  const int col = lane & 15;        // this lane's query row within a 16-row group
+  const int quad = lane >> 4;       // which k slots (and output rows of D) the lane holds
+
+  // Staging roles. K: 16-byte chunk sc of tile tokens st + 16 i (i = 0..3), one per page.
+  // V: chunk sc (d = 8 sc .. 8 sc + 7) of tile tokens 4 st .. 4 st + 3, all in page st / 4.
+  const int sc = tid & 15;
+  const int st = tid >> 4;
+  const char* kbase = static_cast<const char*>(a.k_pages) + static_cast<size_t>(g) * kPageBytes + sc * 16;
+  const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageBytes + sc * 16;
+  const size_t page_stride = static_cast<size_t>(a.n_kv_heads) * kPageBytes;
 
   for (int mb = blockIdx.x; mb * kRowsPerBlock < rows_total; mb += gridDim.x) {
-    // ---- this wave's 16 rows: row r = chunk token r / G, head r % G
-    const int row = mb * kRowsPerBlock + wave * kRowsPerWave + col;
-    const bool live = row < rows_total;
-    const int tok = live ? row / kGroup : 0;
-    const int h = live ? row % kGroup : 0;
-    const int pos = live && !bad ? L - C + tok : -1;      // last visible token of the row
-    const size_t q_off = (static_cast<size_t>(r0 + tok) * hq + g * kGroup + h) * kHeadDim;
-    // Q^T as the B operand: lane holds Q[row][16 kb + 4 quad + e], kb = 0..7.
-    h4 qb[8];
+    const int wrow0 = mb * kRowsPerBlock + wave * kRowsPerWave;
+    // ---- this wave's rows: row r = chunk token r / G, head r % G; lane holds row col of
+    // each group. Q^T as the B operand: Q[row][32 kb + 8 quad + e].
+    h8 qb[kRowGroups][4];
+    int pos[kRowGroups];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-      if (live) {
-        const uint2 w = *reinterpret_cast<const uint2*>(
-            static_cast<const _Float16*>(a.q) + q_off + 16 * kb + 4 * quad);
-        qb[kb] = __builtin_bit_cast(h4, w);
-      } else {
-        qb[kb] = h4{0, 0, 0, 0};
+    for (int grp = 0; grp < kRowGroups; ++grp) {
+      const int row = wrow0 + 16 * grp + col;
+      const bool live = row < rows_total;
+      const int tok = live ? row / kGroup : 0;
+      const int h = live ? row % kGroup : 0;
+      pos[grp] = live && !bad ? L - C + tok : -1;      // last visible token of the row
+      const _Float16* qp = static_cast<const _Float16*>(a.q) +
+                           (static_cast<size_t>(r0 + tok) * hq + g * kGroup + h) * kHeadDim + 8 * quad;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if (live) {
+          qb[grp][kb] = __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(qp + 32 * kb));
+        } else {
+          qb[grp][kb] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
       }
     }
-    // Last page any row of this block reads.
+    // Tiles this block reads (up to its last row's position), and the last position of
+    // this wave's rows (tiles past it need no arithmetic from this wave).
     const int last_row = min(rows_total, (mb + 1) * kRowsPerBlock) - 1;
     const int last_pos = bad ? -1 : L - C + last_row / kGroup;
-    const int pages = bad ? 0 : last_pos / kBlockSize + 1;
+    const int tiles = (last_pos + kTileTok) / kTileTok;
+    const int wave_last_row = min(rows_total, wrow0 + kRowsPerWave) - 1;
+    const int wave_last_pos = (bad || wave_last_row < wrow0) ? -1 : L - C + wave_last_row / kGroup;
 
-    float m = kNegInfPf, l = 0.0f;                // softmax state of row `col`
-    f4 o[8];                                      // O[4 quad + e][16 db + col]
+    float m[kRowGroups], l[kRowGroups];           // running max (log2 units) and this lane's sum
+    f4 o[kRowGroups][8];                          // O^T[16 db + 4 quad + e][row col]
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int grp = 0; grp < kRowGroups; ++grp) {
+      m[grp] = kNegInfPf;
+      l[grp] = 0.0f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[grp][db] = f4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    // Staging: thread t moves 16 bytes of each tile: token t / 16, bytes 16 (t % 16). Slots
-    // past L_b in the last page are stored as zeros (they may hold anything, NaN included,
-    // and a zero weight times NaN would still be NaN in P V); their loads re-read the last
-    // valid row, whose cache lines are fetched anyway.
-    const int st_tok = tid >> 4;
-    const int st_col = (tid & 15) * 16;
-    auto fetch = [&](int j, u32x4& kr, u32x4& vr) __attribute__((always_inline)) {
-      const int phys = a.block_table[static_cast<size_t>(b) * a.max_blocks + j];
-      const size_t base = (static_cast<size_t>(phys) * a.n_kv_heads + g) * (kBlockSize * kHeadDim * 2);
-      const int valid = L - j * kBlockSize;          // >= 1 for every page read
-      const int tok = min(st_tok, valid - 1);
-      kr = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.k_pages) + base + tok * 256 + st_col);
-      vr = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.v_pages) + base + tok * 256 + st_col);
-      if (st_tok >= valid) kr = vr = u32x4{0u, 0u, 0u, 0u};
+    // Loads of tile j into registers. Tokens at or past L_b load the last valid row instead
+    // (its cache lines are fetched anyway) and are staged as zeros: their slots may hold
+    // anything, NaN included, and a zero weight times NaN would still be NaN in P V.
+    u32x4 kr[4], vr[4];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+      const int last_slot = (L - 1) % kBlockSize;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int page = kPagesPerTile * j + i;
+        const int t = page * kBlockSize + st;
+        const int phys = table[min(page, nb - 1)];
+        const int slot = t < L ? st : last_slot;
+        kr[i] = *reinterpret_cast<const u32x4*>(kbase + phys * page_stride + slot * (kHeadDim * 2));
+        if (t >= L) kr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      const int vpage = kPagesPerTile * j + (st >> 2);
+      const int vphys = table[min(vpage, nb - 1)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = kTileTok * j + 4 * st + e;
+        const int slot = t < L ? (4 * st + e) % kBlockSize : last_slot;
+        vr[e] = *reinterpret_cast<const u32x4*>(vbase + vphys * page_stride + slot * (kHeadDim * 2));
+        if (t >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
+      }
     };
-    u32x4 kr, vr;
-    if (pages > 0) fetch(0, kr, vr);
-    for (int j = 0; j < pages; ++j) {
-      __syncthreads();   // the previous page is no longer read
-      *reinterpret_cast<u32x4*>(s_k + st_tok * kTileStride + st_col) = kr;
-      *reinterpret_cast<u32x4*>(s_v + st_tok * kTileStride + st_col) = vr;
+    if (tiles > 0) fetch(0);
+    for (int j = 0; j < tiles; ++j) {
+      __syncthreads();   // the previous tile is no longer read
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(s_k + (st + 16 * i) * kKStride + sc * 16) = kr[i];
+      // V^T[8 sc + x][4 st .. 4 st + 3]: element x of each of the four token rows.
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int w = x >> 1;
+        uint32_t lo, hi;
+        if (x & 1) {
+          lo = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
+          hi = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
+        } else {
+          lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
+          hi = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
+        }
+        *reinterpret_cast<u32x2*>(s_vt + (8 * sc + x) * kVtStride + 8 * st) = u32x2{lo, hi};
+      }
       __syncthreads();
-      if (j + 1 < pages) fetch(j + 1, kr, vr);
+      if (j + 1 < tiles) fetch(j + 1);
+      if (kTileTok * j > wave_last_pos) continue;   // every row of this wave ends earlier
 
-      // S^T = K Q^T over d = 128 in 8 steps of 16.
-      f4 s = f4{0.f, 0.f, 0.f, 0.f};
+      // S^T for the tile's four 16-token subtiles, both row groups; each K operand is read
+      // once from LDS and used for both groups.
+      f4 s[kRowGroups][4];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const uint2 w = *reinterpret_cast<const uint2*>(s_k + col * kTileStride + (16 * kb + 4 * quad) * 2);
-        s = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, w), qb[kb], s, 0, 0, 0);
+      for (int sb = 0; sb < 4; ++sb) {
+        s[0][sb] = f4{0.f, 0.f, 0.f, 0.f};
+        s[1][sb] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const h8 ka = __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(
+              s_k + (16 * sb + col) * kKStride + (32 * kb + 8 * quad) * 2));
+          s[0][sb] = mfma32(ka, qb[0][kb], s[0][sb]);
+          s[1][sb] = mfma32(ka, qb[1][kb], s[1][sb]);
+        }
       }
-      // Lane holds S[row col][token 16 j + 4 quad + e]. Online softmax for row `col`.
-      float sv[4];
-      float mx = kNegInfPf;
+      // Online softmax per row: lane holds S[row col][tile token 16 sb + 4 quad + e].
+      h8 pb[kRowGroups][2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = j * kBlockSize + 4 * quad + e;
-        sv[e] = t <= pos ? s[e] * a.scale_log2 : kNegInfPf;
-        mx = fmaxf(mx, sv[e]);
+      for (int grp = 0; grp < kRowGroups; ++grp) {
+        float mx = kNegInfPf;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int t = kTileTok * j + 16 * sb + 4 * quad + e;
+            const float v = t <= pos[grp] ? s[grp][sb][e] * a.scale_log2 : kNegInfPf;
+            s[grp][sb][e] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m[grp], mx);
+        const float base = m_new == kNegInfPf ? 0.0f : m_new;
+        const float alpha = exp2_fast(m[grp] - base);
+        float sum = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = exp2_fast(s[grp][sb][e] - base);
+            sum += p;
+            pb[grp][sb >> 1][4 * (sb & 1) + e] = static_cast<_Float16>(p);
+          }
+        }
+        l[grp] = l[grp] * alpha + sum;
+        m[grp] = m_new;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[grp][db] *= alpha;
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float base = m_new == kNegInfPf ? 0.0f : m_new;
-      const float alpha = exp2_fast(m - base);
-      float p[4], sum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = exp2_fast(sv[e] - base);
-        sum += p[e];
-      }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
-      l = l * alpha + sum;
-      m = m_new;
-      // Rescale O: its rows are 4 quad + e, whose alpha sits in lane 4 quad + e.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ae = __shfl(alpha, 4 * quad + e);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][e] *= ae;
-      }
-      // O += P V: P[row col][token 4 quad + e] is already the A operand's layout.
-      const h4 pa = h4{static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1]),
-                       static_cast<_Float16>(p[2]), static_cast<_Float16>(p[3])};
+      // O^T += V^T P^T over the tile's two 32-token halves.
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        h4 vb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vb[e] = *reinterpret_cast<const _Float16*>(s_v + (4 * quad + e) * kTileStride + (16 * db + col) * 2);
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, vb, o[db], 0, 0, 0);
+        for (int c = 0; c < 2; ++c) {
+          const unsigned char* vp = s_vt + (16 * db + col) * kVtStride + (32 * c + 4 * quad) * 2;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 32);
+          const h8 va = __builtin_bit_cast(h8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[0][db] = mfma32(va, pb[0][c], o[0][db]);
+          o[1][db] = mfma32(va, pb[1][c], o[1][db]);
+        }
       }
     }
 
-    // Normalise and store: lane holds O[row 4 quad + e][d = 16 db + col].
+    // Normalise and store: lane holds O[row col][d = 16 db + 4 quad + e], four consecutive d.
     const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = mb * kRowsPerBlock + wave * kRowsPerWave + 4 * quad + e;
-      const float le = __shfl(l, 4 * quad + e);
-      if (r >= rows_total) continue;
-      const int rt = r / kGroup;
-      const int rh = r % kGroup;
-      float* dst = a.out + (static_cast<size_t>(r0 + rt) * hq + g * kGroup + rh) * kHeadDim;
+    for (int grp = 0; grp < kRowGroups; ++grp) {
+      float lt = l[grp];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const int row = wrow0 + 16 * grp + col;
+      if (row >= rows_total) continue;
+      const float inv = 1.0f / lt;
+      float* dst = a.out + (static_cast<size_t>(r0 + row / kGroup) * hq + g * kGroup + row % kGroup) * kHeadDim +
+                   4 * quad;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) dst[16 * db + col] = bad ? nan : o[db][e] / le;
+      for (int db = 0; db < 8; ++db) {
+        const f4 v = bad ? f4{nan, nan, nan, nan} : o[grp][db] * inv;
+        *reinterpret_cast<f4*>(dst + 16 * db) = v;
+      }
     }
   }
 }
