@@ -421,7 +421,7 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
       static_cast<long long>(batch) * max_blocks_per_seq > INT_MAX ||
       static_cast<long long>(num_pages) * n_kv_heads > UINT32_MAX ||
       static_cast<long long>(max_chunk) * group > INT_MAX ||
-      batch > 65535 || n_kv_heads > 65535)                       // grid dimensions
+      static_cast<long long>(batch) * n_kv_heads >= (1LL << 24))   // one-dimensional grid
     return DECODE_ATTN_ERR_UNSUPPORTED;
   if (batch == 0) return DECODE_ATTN_OK;
   (void)hipGetLastError();  // start from a clean error state

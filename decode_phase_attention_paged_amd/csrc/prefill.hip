@@ -26,6 +26,7 @@
 // and 32c + 16 + 4q + (e - 4) (e >= 4), which is how the first product's output falls.
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -44,6 +45,11 @@ constexpr int kKStride = kHeadDim * 2 + 16;           // LDS bytes per K token r
 constexpr int kVtStride = kTileTok * 2 + 8;           // LDS bytes per V^T d row (padded)
 constexpr int kPageBytes = kBlockSize * kHeadDim * 2; // one (page, KV head) fp16 tile
 constexpr float kNegInfPf = -__builtin_huge_valf();
+constexpr int kOrderMaxPf = kPfThreads;              // batches ranked longest-first in-kernel
+constexpr int kXcds = 8;                              // gfx950 dies; workgroup i runs on die i % 8
+// The running max only moves when a tile's max exceeds it by more than this (log2 units),
+// so the weights stay below 2^8 (exact to fp16's precision) and most tiles skip the rescale.
+constexpr float kLazyRescale = 8.0f;
 
 static_assert(kPagesPerTile * kBlockSize == kTileTok, "tiles are whole pages");
 static_assert(kTileTok * kHeadDim * 2 == kPfThreads * 4 * 16, "four 16-byte K loads per thread");
@@ -60,20 +66,56 @@ __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
 }
 
 // One workgroup: query-row block mb of (sequence b, KV head g), looping over further blocks
-// gridDim.x apart.
+// `nx` apart. The grid is one-dimensional, nx * Hkv * B workgroups. Work order: for batches
+// of up to 256 sequences the (sequence, KV head) pairs are taken longest sequence first
+// (every workgroup ranks the lengths itself, ties by index), and each pair's row blocks
+// last rows first, since later rows see more of the cache. When the pair count is a
+// multiple of the die count, all row blocks of a pair run on one die, so its K/V pages are
+// fetched into that die's L2 once.
 template <int kGroup>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_kernel(PrefillArgs a) {
+void prefill_kernel(PrefillArgs a, int nx) {
   __shared__ __attribute__((aligned(16))) unsigned char s_k[kTileTok * kKStride];
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[kHeadDim * kVtStride];
+  __shared__ int s_len[kOrderMaxPf];
   __shared__ int s_bad;
+  __shared__ int s_pick;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
   const int hq = a.n_kv_heads * kGroup;
+  const int pairs = a.batch * a.n_kv_heads;
+
+  const int id = blockIdx.x;
+  int pair, mbx;
+  if (pairs % kXcds == 0) {
+    const int k = id / kXcds;
+    pair = id % kXcds + kXcds * (k / nx);
+    mbx = k % nx;
+  } else {
+    pair = id / nx;
+    mbx = id % nx;
+  }
+  mbx = nx - 1 - mbx;
+  const int g = pair % a.n_kv_heads;
+  const int rank = pair / a.n_kv_heads;
+  int b = rank;
+  if (a.batch <= kOrderMaxPf) {
+    const int my = tid < a.batch ? a.seq_lens[tid] : 0;
+    s_len[tid] = my;
+    __syncthreads();
+    if (tid < a.batch) {
+      int r = 0;
+      for (int t = 0; t < a.batch; ++t) {
+        const int o = s_len[t];
+        r += (o > my) | ((o == my) & (t < tid));
+      }
+      if (r == rank) s_pick = tid;
+    }
+    __syncthreads();
+    b = s_pick;
+  }
 
   const int L = a.seq_lens[b];
   const int r0 = a.q_start[b];
@@ -96,6 +138,11 @@ void prefill_kernel(PrefillArgs a) {
   const bool bad = s_bad != 0;
 
   const int rows_total = C * kGroup;
+  // Scores are scaled by ssc >= FLT_MIN (a zero scale gives the same weights as the
+  // smallest normal one), so a masked -inf score stays -inf through the fma.
+  const float ssc = fmaxf(fabsf(a.scale_log2), __FLT_MIN__);
+  const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const u32x4 qflip = u32x4{qsign, qsign, qsign, qsign};
   const int col = lane & 15;        // this lane's query row within a 16-row group
   const int quad = lane >> 4;       // which k slots (and output rows of D) the lane holds
 
@@ -107,25 +154,31 @@ void prefill_kernel(PrefillArgs a) {
   const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageBytes + sc * 16;
   const size_t page_stride = static_cast<size_t>(a.n_kv_heads) * kPageBytes;
 
-  for (int mb = blockIdx.x; mb * kRowsPerBlock < rows_total; mb += gridDim.x) {
+  for (int mb = mbx; mb * kRowsPerBlock < rows_total; mb += nx) {
     const int wrow0 = mb * kRowsPerBlock + wave * kRowsPerWave;
     // ---- this wave's rows: row r = chunk token r / G, head r % G; lane holds row col of
     // each group. Q^T as the B operand: Q[row][32 kb + 8 quad + e].
+    // A negative scale is applied as |scale| to -q (exact), so that the largest score is the
+    // largest product and the scale folds into one fma per score.
     h8 qb[kRowGroups][4];
-    int pos[kRowGroups];
+    int pos[kRowGroups];        // last visible token of the lane's row (-1: none)
+    int diag_from[kRowGroups];  // last visible token of the group's first row
 #pragma unroll
     for (int grp = 0; grp < kRowGroups; ++grp) {
       const int row = wrow0 + 16 * grp + col;
       const bool live = row < rows_total;
       const int tok = live ? row / kGroup : 0;
       const int h = live ? row % kGroup : 0;
-      pos[grp] = live && !bad ? L - C + tok : -1;      // last visible token of the row
+      pos[grp] = live && !bad ? L - C + tok : -1;
+      const int first = wrow0 + 16 * grp;
+      diag_from[grp] = first < rows_total ? L - C + first / kGroup : INT_MAX;
       const _Float16* qp = static_cast<const _Float16*>(a.q) +
                            (static_cast<size_t>(r0 + tok) * hq + g * kGroup + h) * kHeadDim + 8 * quad;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if (live) {
-          qb[grp][kb] = __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(qp + 32 * kb));
+          const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * kb);
+          qb[grp][kb] = __builtin_bit_cast(h8, w ^ qflip);
         } else {
           qb[grp][kb] = h8{0, 0, 0, 0, 0, 0, 0, 0};
         }
@@ -150,8 +203,9 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // Loads of tile j into registers. Tokens at or past L_b load the last valid row instead
-    // (its cache lines are fetched anyway) and are staged as zeros: their slots may hold
-    // anything, NaN included, and a zero weight times NaN would still be NaN in P V.
+    // (its cache lines are fetched anyway): their slots may hold anything, NaN included.
+    // Their scores are masked, and their V rows are staged as zeros, since a zero weight
+    // times NaN would still be NaN in P V.
     u32x4 kr[4], vr[4];
     auto fetch = [&](int j) __attribute__((always_inline)) {
       const int last_slot = (L - 1) % kBlockSize;
@@ -162,7 +216,6 @@ void prefill_kernel(PrefillArgs a) {
         const int phys = table[min(page, nb - 1)];
         const int slot = t < L ? st : last_slot;
         kr[i] = *reinterpret_cast<const u32x4*>(kbase + phys * page_stride + slot * (kHeadDim * 2));
-        if (t >= L) kr[i] = u32x4{0u, 0u, 0u, 0u};
       }
       const int vpage = kPagesPerTile * j + (st >> 2);
       const int vphys = table[min(vpage, nb - 1)];
@@ -171,7 +224,11 @@ void prefill_kernel(PrefillArgs a) {
         const int t = kTileTok * j + 4 * st + e;
         const int slot = t < L ? (4 * st + e) % kBlockSize : last_slot;
         vr[e] = *reinterpret_cast<const u32x4*>(vbase + vphys * page_stride + slot * (kHeadDim * 2));
-        if (t >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
+      }
+      if (kTileTok * (j + 1) > L) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kTileTok * j + 4 * st + e >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
       }
     };
     if (tiles > 0) fetch(0);
@@ -213,42 +270,54 @@ void prefill_kernel(PrefillArgs a) {
           s[1][sb] = mfma32(ka, qb[1][kb], s[1][sb]);
         }
       }
-      // Online softmax per row: lane holds S[row col][tile token 16 sb + 4 quad + e].
+      // Online softmax per row: lane holds S[row col][tile token 16 sb + 4 quad + e]. Only
+      // tiles that reach past a group's first row's last visible token need the causal mask.
+      // The reference max m moves only when a row's tile max exceeds it by more than
+      // kLazyRescale (then O and l are rescaled); otherwise the weights exp2(s ssc - m) stay
+      // below 2^kLazyRescale. The final normalisation divides both by the same sum, so the
+      // result is the softmax whatever reference is used.
       h8 pb[kRowGroups][2];
 #pragma unroll
       for (int grp = 0; grp < kRowGroups; ++grp) {
+        if (kTileTok * j + kTileTok - 1 > diag_from[grp]) {
+          const int lim = pos[grp] - (kTileTok * j + 4 * quad);
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (16 * sb + e > lim) s[grp][sb][e] = kNegInfPf;
+          }
+        }
         float mx = kNegInfPf;
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = kTileTok * j + 16 * sb + 4 * quad + e;
-            const float v = t <= pos[grp] ? s[grp][sb][e] * a.scale_log2 : kNegInfPf;
-            s[grp][sb][e] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[grp][sb][e]);
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m[grp], mx);
-        const float base = m_new == kNegInfPf ? 0.0f : m_new;
-        const float alpha = exp2_fast(m[grp] - base);
+        mx *= ssc;
+        const bool grow = mx > m[grp] + kLazyRescale;
+        if (__ballot(grow)) {
+          const float m_new = grow ? mx : m[grp];
+          const float alpha = grow ? exp2_fast(m[grp] - m_new) : 1.0f;
+          l[grp] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[grp][db] *= alpha;
+          m[grp] = m_new;
+        }
+        const float mu = m[grp] == kNegInfPf ? 0.0f : m[grp];
         float sum = 0.0f;
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float p = exp2_fast(s[grp][sb][e] - base);
+            const float p = exp2_fast(__builtin_fmaf(s[grp][sb][e], ssc, -mu));
             sum += p;
             pb[grp][sb >> 1][4 * (sb & 1) + e] = static_cast<_Float16>(p);
           }
         }
-        l[grp] = l[grp] * alpha + sum;
-        m[grp] = m_new;
-        if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-          for (int db = 0; db < 8; ++db) o[grp][db] *= alpha;
-        }
+        l[grp] += sum;
       }
       // O^T += V^T P^T over the tile's two 32-token halves.
 #pragma unroll
@@ -289,14 +358,20 @@ void prefill_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill(int group, const PrefillArgs& a, int max_chunk, hipStream_t stream) {
-  const long long blocks = (static_cast<long long>(max_chunk) * group + kRowsPerBlock - 1) / kRowsPerBlock;
-  const dim3 grid(static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 65535 ? 65535 : blocks)),
-                  static_cast<unsigned>(a.n_kv_heads), static_cast<unsigned>(a.batch));
+  // nx row blocks per (sequence, KV head); workgroups loop over the rest of a longer chunk.
+  // The grid stays below 2^24 workgroups (2^32 work-items).
+  const long long pairs = static_cast<long long>(a.batch) * a.n_kv_heads;
+  const long long want = (static_cast<long long>(max_chunk) * group + kRowsPerBlock - 1) / kRowsPerBlock;
+  const long long cap = ((1LL << 24) - 1) / pairs;
+  const long long nx = want < 1 ? 1 : (want > cap ? cap : want);
+  if (nx < 1) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(nx * pairs));
+  const int nxi = static_cast<int>(nx);
   switch (group) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPfThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPfThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
+    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
+    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
+    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

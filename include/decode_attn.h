@@ -253,7 +253,7 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
  * longer than L_b, whose L_b exceeds the table, or whose table holds a page id outside
  * [0, num_pages) among its first ceil(L_b / block_size) entries gets NaN in all its rows.
  * Supported: kv_dtype FP16 (others return DECODE_ATTN_ERR_UNSUPPORTED), head_dim 128,
- * block_size 16, G in {1, 2, 4, 8}, batch and n_kv_heads up to 65535. Asynchronous on
+ * block_size 16, G in {1, 2, 4, 8}, batch * n_kv_heads below 2^24. Asynchronous on
  * `stream`; never allocates; capturable in a HIP graph. Returns a decode_attn_status.
  */
 int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pages,

@@ -298,7 +298,7 @@ def call_prefill(lib, **over):
     (dict(out=None), 1),
     (dict(q=A + 8), 1),                      # q not 16-byte aligned
     (dict(out=7 * A + 4), 1),
-    (dict(batch=70000), 2),                  # beyond the grid's z range
+    (dict(batch=1 << 23), 2),                # batch x Hkv = 2^24: beyond the grid
     (dict(batch=-1), 1),
     (dict(batch=0, q=None, qs=None, k=None, v=None, bt=None, sl=None, out=None), 0),
     (dict(total=0, q=None, out=None, batch=0), 0),

@@ -136,3 +136,45 @@ def test_full_size_preset_on_sampled_sequences(torch, lib):
         ref = oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
                                        w.seq_lens[b:b + 1], sub_start, w.scale)[0]
         assert_parity(got[rows], ref, f"preset sequence {b}")
+
+
+@pytest.mark.parametrize("batch,hkv", [(4, 2), (8, 1), (3, 8)])
+def test_work_orders(torch, lib, batch, hkv):
+    # Pair counts that are multiples of 8 run every row block of a (sequence, KV head) on
+    # one die; the others run in rank order only. Lengths with ties check the ranking.
+    cfg = SMALL.with_(batch=batch, n_q_heads=4 * hkv, n_kv_heads=hkv, len_lo=20, len_hi=330)
+    rng = np.random.default_rng(300 + batch)
+    lens = rng.integers(20, 331, size=batch).astype(np.int32)
+    lens[batch // 2] = lens[0]
+    w = generate(cfg, seed=301, poison=True, seq_lens=lens)
+    q_start = chunk_layout(w.seq_lens, rng)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print(f"case prefill order batch={batch} hkv={hkv} lens={w.seq_lens.tolist()}", flush=True)
+    got = run(torch, lib, w, q, q_start, max_chunk=int(np.diff(q_start).max()))
+    assert_parity(got, reference(w, q, q_start), f"order {batch}x{hkv}")
+
+
+def test_batch_beyond_the_ranked_order(torch, lib):
+    # More than 256 sequences: the workgroups take pairs in index order.
+    cfg = SMALL.with_(batch=300, n_q_heads=4, n_kv_heads=1, len_lo=1, len_hi=40)
+    w = generate(cfg, seed=302)
+    rng = np.random.default_rng(302)
+    q_start = chunk_layout(w.seq_lens, rng)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print("case prefill batch 300", flush=True)
+    got = run(torch, lib, w, q, q_start)
+    assert_parity(got, reference(w, q, q_start), "batch 300")
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.5])
+def test_scales(torch, lib, scale):
+    # A negative scale runs as |scale| on -q; a zero scale gives uniform weights; a large
+    # one makes peaky rows whose reference max moves often.
+    cfg = SMALL.with_(batch=3, n_q_heads=8, n_kv_heads=2, len_lo=60, len_hi=260, scale=scale)
+    w = generate(cfg, seed=303)
+    rng = np.random.default_rng(303)
+    q_start = chunk_layout(w.seq_lens, rng)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print(f"case prefill scale={scale}", flush=True)
+    got = run(torch, lib, w, q, q_start)
+    assert_parity(got, reference(w, q, q_start), f"scale {scale}")
