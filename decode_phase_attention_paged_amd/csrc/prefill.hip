@@ -61,6 +61,21 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Read-only load through the scalar cache (constant address space), for values every lane
+// of the workgroup shares.
+__device__ __forceinline__ int32_t scalar_load_pf(const int32_t* base, int idx) {
+  typedef const __attribute__((address_space(4))) int32_t* ConstPtr;
+  return ((ConstPtr)(base))[idx];
+}
+
+// Byte offset of V^T[d][token] in the staged tile: rows of kVtStride bytes; the 4-token
+// granules of rows with bit 4 of d set are XOR-swizzled by 4 granules, so that the staging
+// writes (16 lanes: four token granules x four d chunks) and the operand reads (16 lanes:
+// sixteen consecutive d) both fall on distinct banks.
+__device__ __forceinline__ int vt_offset(int d, int granule) {
+  return d * kVtStride + 8 * (granule ^ (4 * ((d >> 4) & 1)));
+}
+
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -146,12 +161,15 @@ void prefill_kernel(PrefillArgs a, int nx) {
   const int col = lane & 15;        // this lane's query row within a 16-row group
   const int quad = lane >> 4;       // which k slots (and output rows of D) the lane holds
 
-  // Staging roles. K: 16-byte chunk sc of tile tokens st + 16 i (i = 0..3), one per page.
-  // V: chunk sc (d = 8 sc .. 8 sc + 7) of tile tokens 4 st .. 4 st + 3, all in page st / 4.
+  // Staging roles. K: 16-byte chunk sc of tile tokens st + 16 i (i = 0..3), slot st of the
+  // tile's page i. V: wave w stages the tile's page w; lane (vs, vc) moves 16-byte chunk vc
+  // (d = 8 vc .. 8 vc + 7) of the page's tokens 4 vs .. 4 vs + 3.
   const int sc = tid & 15;
   const int st = tid >> 4;
-  const char* kbase = static_cast<const char*>(a.k_pages) + static_cast<size_t>(g) * kPageBytes + sc * 16;
-  const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageBytes + sc * 16;
+  const int vs = lane & 3;
+  const int vc = lane >> 2;
+  const char* kbase = static_cast<const char*>(a.k_pages) + static_cast<size_t>(g) * kPageBytes;
+  const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageBytes;
   const size_t page_stride = static_cast<size_t>(a.n_kv_heads) * kPageBytes;
 
   for (int mb = mbx; mb * kRowsPerBlock < rows_total; mb += nx) {
@@ -209,26 +227,28 @@ void prefill_kernel(PrefillArgs a, int nx) {
     u32x4 kr[4], vr[4];
     auto fetch = [&](int j) __attribute__((always_inline)) {
       const int last_slot = (L - 1) % kBlockSize;
+      // Page ids of the tile's four pages: uniform, through the scalar cache.
+      int phys[kPagesPerTile];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int page = kPagesPerTile * j + i;
-        const int t = page * kBlockSize + st;
-        const int phys = table[min(page, nb - 1)];
-        const int slot = t < L ? st : last_slot;
-        kr[i] = *reinterpret_cast<const u32x4*>(kbase + phys * page_stride + slot * (kHeadDim * 2));
+      for (int i = 0; i < kPagesPerTile; ++i) phys[i] = scalar_load_pf(table, min(kPagesPerTile * j + i, nb - 1));
+#pragma unroll
+      for (int i = 0; i < kPagesPerTile; ++i) {
+        const int t = (kPagesPerTile * j + i) * kBlockSize + st;
+        const uint32_t off = (t < L ? st : last_slot) * (kHeadDim * 2) + sc * 16;
+        kr[i] = *reinterpret_cast<const u32x4*>(kbase + phys[i] * page_stride + off);
       }
-      const int vpage = kPagesPerTile * j + (st >> 2);
-      const int vphys = table[min(vpage, nb - 1)];
+      const int vphys = wave == 0 ? phys[0] : wave == 1 ? phys[1] : wave == 2 ? phys[2] : phys[3];
+      const char* vpage = vbase + vphys * page_stride;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = kTileTok * j + 4 * st + e;
-        const int slot = t < L ? (4 * st + e) % kBlockSize : last_slot;
-        vr[e] = *reinterpret_cast<const u32x4*>(vbase + vphys * page_stride + slot * (kHeadDim * 2));
+        const int t = kTileTok * j + kBlockSize * wave + 4 * vs + e;
+        const uint32_t off = (t < L ? 4 * vs + e : last_slot) * (kHeadDim * 2) + vc * 16;
+        vr[e] = *reinterpret_cast<const u32x4*>(vpage + off);
       }
       if (kTileTok * (j + 1) > L) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (kTileTok * j + 4 * st + e >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
+          if (kTileTok * j + kBlockSize * wave + 4 * vs + e >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
       }
     };
     if (tiles > 0) fetch(0);
@@ -237,7 +257,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4*>(s_k + (st + 16 * i) * kKStride + sc * 16) = kr[i];
-      // V^T[8 sc + x][4 st .. 4 st + 3]: element x of each of the four token rows.
+      // V^T[8 vc + x][tile tokens 16 w + 4 vs .. + 3]: element x of each of the four rows.
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int w = x >> 1;
@@ -249,7 +269,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
           lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
           hi = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
         }
-        *reinterpret_cast<u32x2*>(s_vt + (8 * sc + x) * kVtStride + 8 * st) = u32x2{lo, hi};
+        *reinterpret_cast<u32x2*>(s_vt + vt_offset(8 * vc + x, 4 * wave + vs)) = u32x2{lo, hi};
       }
       __syncthreads();
       if (j + 1 < tiles) fetch(j + 1);
@@ -324,9 +344,9 @@ void prefill_kernel(PrefillArgs a, int nx) {
       for (int db = 0; db < 8; ++db) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const unsigned char* vp = s_vt + (16 * db + col) * kVtStride + (32 * c + 4 * quad) * 2;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 32);
+          const int d = 16 * db + col;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + quad));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + 4 + quad));
           const h8 va = __builtin_bit_cast(h8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           o[0][db] = mfma32(va, pb[0][c], o[0][db]);
           o[1][db] = mfma32(va, pb[1][c], o[1][db]);
