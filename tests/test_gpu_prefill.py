@@ -178,3 +178,59 @@ def test_scales(torch, lib, scale):
     print(f"case prefill scale={scale}", flush=True)
     got = run(torch, lib, w, q, q_start)
     assert_parity(got, reference(w, q, q_start), f"scale {scale}")
+
+
+def test_graph_replays_match_eager(torch, lib):
+    # The prefill launches one kernel and allocates nothing, so a captured call replays: with
+    # new chunk rows copied in before each replay and an eager call in between, every replay
+    # must give the eager call's bit pattern and match the oracle.
+    cfg = SMALL.with_(batch=4, len_lo=30, len_hi=300)
+    w = generate(cfg, seed=304, poison=True)
+    rng = np.random.default_rng(304)
+    q_start = chunk_layout(w.seq_lens, rng)
+    shape = (int(q_start[-1]), cfg.n_q_heads, 128)
+    t = lambda a: dev_tensor(torch, a)
+    d = dict(q=t(rng.standard_normal(shape).astype(np.float16)), q_start=t(q_start),
+             k_pages=t(w.k_pages), v_pages=t(w.v_pages), block_table=t(w.block_table),
+             seq_lens=t(w.seq_lens))
+    out = torch.zeros(shape, dtype=torch.float32, device="cuda:0")
+    eager = torch.empty_like(out)
+
+    def call(dst):
+        lib.decode_attn_prefill(d["q"], d["q_start"], d["k_pages"], d["v_pages"],
+                                d["block_table"], d["seq_lens"], w.scale, out=dst)
+
+    print("case prefill graph", flush=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)                                    # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        q_new = rng.standard_normal(shape).astype(np.float16)
+        d["q"].copy_(t(q_new))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        call(eager)                                  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(got, eager.cpu().numpy()), f"replay {replay}: out differs"
+        assert_parity(got, reference(w, q_new, q_start), f"prefill graph replay {replay}")
+
+
+def test_deterministic(torch, lib):
+    # The same inputs give the same bits: the kernel has no atomics and a fixed order.
+    cfg = SMALL.with_(batch=6, len_lo=50, len_hi=400, n_q_heads=16, n_kv_heads=4)
+    w = generate(cfg, seed=305)
+    rng = np.random.default_rng(305)
+    q_start = chunk_layout(w.seq_lens, rng)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
+    print("case prefill determinism", flush=True)
+    first = run(torch, lib, w, q, q_start)
+    second = run(torch, lib, w, q, q_start)
+    assert np.array_equal(first, second)
