@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--graph", type=int, default=0,
                     help="capture this many consecutive steps in one HIP graph and time "
                          "replays of it (the step count is rounded up to a multiple)")
+    ap.add_argument("--kv", choices=["fp16", "bf16", "int8", "fp8"], default=None,
+                    help="prefill only: run the preset's shapes over another storage format")
     ap.add_argument("--op", choices=["attn", "append", "prefill"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
                          "that precedes it in a decode step, on the same workload; prefill: "
@@ -504,7 +506,7 @@ def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
         sub = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
         t0 = time.perf_counter()
         oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
-                                 w.seq_lens[b:b + 1], sub, w.scale)
+                                 w.seq_lens[b:b + 1], sub, w.scale, w.k_scale, w.v_scale)
         spent += time.perf_counter() - t0
         done_flops += prefill_flops(w.seq_lens[b:b + 1], sub, c.n_q_heads, c.head_dim)
         seqs += 1
@@ -523,6 +525,8 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
     if cfg.chunk <= 0:
         raise SystemExit(f"preset {cfg.name} has no chunk size; use a prefill preset")
     log(f"generating {cfg.name} ...")
+    if args.kv and args.kv != cfg.kv_dtype:
+        cfg = cfg.with_(kv_dtype=args.kv, name=f"{cfg.name}_{args.kv}")
     w = generate(cfg)
     q_host, qs_host = prefill_rows(w)
     flops = prefill_flops(w.seq_lens, qs_host, cfg.n_q_heads, cfg.head_dim)
@@ -534,14 +538,18 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
     reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
     reps = min(reps, max(1, (48 << 30) // pool_bytes))
     pools = [(t(w.k_pages), t(w.v_pages)) for _ in range(reps)]
+    ks, vs = t(w.k_scale), t(w.v_scale)
     out = torch.empty(q_host.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     s_handle = ctypes.c_void_p(stream.cuda_stream)
     p = lambda x: ctypes.c_void_p(x.data_ptr())
     total = q_host.shape[0]
-    call_args = [(p(q), p(qs), p(kp), p(vp), p(bt), p(sl), cfg.batch, total,
+    pz = lambda x: None if x is None else p(x)
+    kv = {"fp16": binding.KV_FP16, "bf16": binding.KV_BF16, "int8": binding.KV_INT8,
+          "fp8": binding.KV_FP8}[cfg.kv_dtype]
+    call_args = [(p(q), p(qs), p(kp), p(vp), pz(ks), pz(vs), p(bt), p(sl), cfg.batch, total,
                   cfg.max_blocks_per_seq, w.num_pages, cfg.n_q_heads, cfg.n_kv_heads,
-                  cfg.head_dim, cfg.block_size, binding.KV_FP16, cfg.chunk, float(w.scale),
+                  cfg.head_dim, cfg.block_size, kv, cfg.chunk, float(w.scale),
                   p(out), s_handle) for kp, vp in pools]
 
     def step(i):
@@ -584,11 +592,12 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
-                   "block_size": cfg.block_size, "chunk": cfg.chunk, "rows": total,
+                   "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype, "chunk": cfg.chunk,
+                   "rows": total,
                    "seq_lens": f"uniform [{cfg.len_lo}, {cfg.len_hi}], seed {w.seed}",
                    "flops_per_step": int(flops), "kv_bytes_per_step": int(w.kv_bytes),
                    "replicas": reps},

@@ -85,8 +85,8 @@ _SIGNATURES = {
                             _P, _I, _I, _P, _SZ, _P]),
     "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "decode_attn_append": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
-    "decode_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
-                                 _F, _P, _P]),
+    "decode_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                 _I, _I, _F, _P, _P]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
 }
@@ -293,14 +293,15 @@ def decode_attn_append(k_new, v_new, block_table, positions, k_pages, v_pages, *
 
 
 def decode_attn_prefill(q, q_start, k_pages, v_pages, block_table, seq_lens, scale, *,
-                        max_chunk: Optional[int] = None, out=None):
+                        k_scale=None, v_scale=None, max_chunk: Optional[int] = None, out=None):
     """Chunked-prefill attention (see decode_attn_prefill in include/decode_attn.h).
 
-    ``q`` holds every sequence's chunk rows stacked (fp16 [T, n_q_heads, head_dim]);
-    sequence b's rows are ``q[q_start[b]:q_start[b+1]]`` (int32 [batch + 1]) and sit at the
-    end of its ``seq_lens[b]`` cached tokens. ``max_chunk`` bounds the chunk sizes for the
-    grid (default: T, always safe). Returns ``out`` (fp32 [T, n_q_heads, head_dim]),
-    enqueued on torch's current stream of q's device."""
+    ``q`` holds every sequence's chunk rows stacked ([T, n_q_heads, head_dim], fp16, or
+    bf16 for a bf16 cache); sequence b's rows are ``q[q_start[b]:q_start[b+1]]`` (int32
+    [batch + 1]) and sit at the end of its ``seq_lens[b]`` cached tokens. int8 and
+    float8_e4m3fn pools take fp32 row scales, as for decode_attn. ``max_chunk`` bounds the
+    chunk sizes for the grid (default: T, always safe). Returns ``out`` (fp32
+    [T, n_q_heads, head_dim]), enqueued on torch's current stream of q's device."""
     lib = load_library()
     dev = q.device
     if dev.type != "cuda":
@@ -309,18 +310,21 @@ def decode_attn_prefill(q, q_start, k_pages, v_pages, block_table, seq_lens, sca
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     named = dict(q=q, q_start=q_start, k_pages=k_pages, v_pages=v_pages,
                  block_table=block_table, seq_lens=seq_lens, out=out)
+    if k_scale is not None or v_scale is not None:
+        named.update(k_scale=k_scale, v_scale=v_scale)
     for name, t in named.items():
+        if t is None:
+            raise ValueError(f"{name} is required")
         if t.device != dev:
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     if k_pages.dim() != 4 or v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
         raise ValueError("k_pages and v_pages must both be [num_pages, n_kv_heads, block_size, head_dim]")
-    kv = _KV_OF_DTYPE.get(k_pages.dtype)
-    if kv is None:
-        raise ValueError("k_pages must be fp16, bf16, int8 or float8_e4m3fn")
-    if q.dtype != torch.float16 or q.dim() != 3:
-        raise ValueError("q must be fp16 [total_rows, n_q_heads, head_dim]")
+    kv = _pool_format(k_pages, k_scale, v_scale)
+    if q.dtype != _row_dtype(kv) or q.dim() != 3:
+        raise ValueError(f"q must be {_row_dtype(kv)} [total_rows, n_q_heads, head_dim] for a "
+                         f"{KV_NAMES[kv]} cache")
     if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must be fp32 [total_rows, n_q_heads, head_dim]")
     batch = seq_lens.shape[0]
@@ -337,8 +341,9 @@ def decode_attn_prefill(q, q_start, k_pages, v_pages, block_table, seq_lens, sca
     chunk = max(1, total if max_chunk is None else int(max_chunk))
     with torch.cuda.device(dev):
         st = lib.decode_attn_prefill(_ptr(q), _ptr(q_start), _ptr(k_pages), _ptr(v_pages),
-                                     _ptr(block_table), _ptr(seq_lens), batch, total,
-                                     block_table.shape[1], num_pages, n_q, n_kv, head_dim,
-                                     block_size, kv, chunk, float(scale), _ptr(out), _stream(dev))
+                                     _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                     _ptr(seq_lens), batch, total, block_table.shape[1],
+                                     num_pages, n_q, n_kv, head_dim, block_size, kv, chunk,
+                                     float(scale), _ptr(out), _stream(dev))
     _check(st, "decode_attn_prefill")
     return out

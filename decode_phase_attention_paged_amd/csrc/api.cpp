@@ -16,7 +16,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (6 << 16) | 1;
+constexpr int kVersion = (6 << 16) | 2;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -395,26 +395,29 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
 }
 
 int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pages,
-                        const void* v_pages, const int32_t* block_table,
-                        const int32_t* seq_lens, int batch, int total_rows,
-                        int max_blocks_per_seq, int num_pages, int n_q_heads, int n_kv_heads,
-                        int head_dim, int block_size, int kv_dtype, int max_chunk, float scale,
-                        float* out, hipStream_t stream) {
+                        const void* v_pages, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, int batch,
+                        int total_rows, int max_blocks_per_seq, int num_pages, int n_q_heads,
+                        int n_kv_heads, int head_dim, int block_size, int kv_dtype, int max_chunk,
+                        float scale, float* out, hipStream_t stream) {
   int st = validate_shapes(batch, max_blocks_per_seq, n_q_heads, n_kv_heads, block_size, 0, 0);
   if (st != DECODE_ATTN_OK) return st;
   if (num_pages < 1 || head_dim < 1 || total_rows < 0 || max_chunk < 1)
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (!known_kv(kv_dtype)) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  const bool scaled = scaled_kv(kv_dtype);
+  if (scaled != (k_scale != nullptr) || scaled != (v_scale != nullptr))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (batch > 0 && (q_start == nullptr || block_table == nullptr || seq_lens == nullptr ||
                     k_pages == nullptr || v_pages == nullptr ||
                     (total_rows > 0 && (q == nullptr || out == nullptr))))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(k_scale, 4) || !aligned(v_scale, 4) ||
       !aligned(q_start, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
       !aligned(out, 16))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (head_dim != kHeadDim || block_size != kBlockSize) return DECODE_ATTN_ERR_UNSUPPORTED;
-  if (kv_dtype != DECODE_ATTN_KV_FP16) return DECODE_ATTN_ERR_UNSUPPORTED;
   const int group = n_q_heads / n_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8) return DECODE_ATTN_ERR_UNSUPPORTED;
   if (static_cast<long long>(max_blocks_per_seq) * block_size > INT_MAX ||
@@ -430,6 +433,8 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
   a.q_start = q_start;
   a.k_pages = k_pages;
   a.v_pages = v_pages;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
@@ -439,7 +444,8 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
   a.num_pages = num_pages;
   a.n_kv_heads = n_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
-  if (dattn::launch_prefill(group, a, max_chunk, stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  if (dattn::launch_prefill(kv_of(kv_dtype), group, a, max_chunk, stream) != hipSuccess)
+    return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
 

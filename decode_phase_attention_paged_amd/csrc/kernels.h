@@ -107,12 +107,14 @@ struct AppendArgs {
 };
 hipError_t launch_append(KvType kv, const AppendArgs& a, hipStream_t stream);
 
-// Chunked-prefill attention over the paged cache (prefill.hip); fp16 K/V.
+// Chunked-prefill attention over the paged cache (prefill.hip).
 struct PrefillArgs {
-  const void* q;               // fp16 [T, Hq, D]: every sequence's chunk rows, stacked
+  const void* q;               // fp16 [T, Hq, D] (bf16 for a bf16 cache): every chunk's rows, stacked
   const int32_t* q_start;      // int32 [B + 1]: sequence b's rows are q_start[b] .. q_start[b+1]-1
-  const void* k_pages;         // fp16 [NP, Hkv, bs, D]
+  const void* k_pages;         // fp16 | bf16 | int8 | fp8 e4m3 [NP, Hkv, bs, D]
   const void* v_pages;
+  const float* k_scale;        // fp32 [NP, Hkv, bs] (int8 and fp8 only)
+  const float* v_scale;
   const int32_t* block_table;  // int32 [B, MB]
   const int32_t* seq_lens;     // int32 [B]: L_b, counting the chunk
   float* out;                  // fp32 [T, Hq, D]
@@ -124,6 +126,6 @@ struct PrefillArgs {
   float scale_log2;            // softmax scale * log2(e)
 };
 // max_chunk bounds C_b for sizing the grid only; longer chunks are still covered.
-hipError_t launch_prefill(int group, const PrefillArgs& a, int max_chunk, hipStream_t stream);
+hipError_t launch_prefill(KvType kv, int group, const PrefillArgs& a, int max_chunk, hipStream_t stream);
 
 }  // namespace dattn

@@ -19,6 +19,13 @@
 // second one takes P^T in, and its result O^T keeps row l % 16 in lane l, so the online-
 // normaliser rescale (fp32, log2 units) is a per-lane multiply with no cross-lane traffic.
 //
+// Storage formats: fp16 K/V with fp16 q on the fp16 matrix cores. bf16 K/V with bf16 q: the
+// scores on the bf16 ones (v_mfma_f32_16x16x32_bf16, exact products), while V is rounded to
+// fp16 when staged, so that the weights of P V keep fp16's 11-bit precision (bf16 weights
+// would carry errors up to 2^-9 of a value). Per-row INT8 and FP8 E4M3 K/V are dequantised
+// while staged (code times its row's fp32 scale, rounded once to fp16) and then take the
+// fp16 path with fp16 q.
+//
 // 16x16x32 operand layout (lane l, q = l / 16, item e): A[l % 16][slot 8q + e] for e < 8,
 // B[slot 8q + e][l % 16], D[4q + e][l % 16] for e < 4. A and B share the slot order, so a
 // contraction is correct for any assignment of the 32 k values to slots, provided A and B
@@ -43,7 +50,6 @@ constexpr int kTileTok = 64;                          // tokens staged per step
 constexpr int kPagesPerTile = kTileTok / kBlockSize;
 constexpr int kKStride = kHeadDim * 2 + 16;           // LDS bytes per K token row (padded)
 constexpr int kVtStride = kTileTok * 2 + 8;           // LDS bytes per V^T d row (padded)
-constexpr int kPageBytes = kBlockSize * kHeadDim * 2; // one (page, KV head) fp16 tile
 constexpr float kNegInfPf = -__builtin_huge_valf();
 constexpr int kOrderMaxPf = kPfThreads;              // batches ranked longest-first in-kernel
 constexpr int kXcds = 8;                              // gfx950 dies; workgroup i runs on die i % 8
@@ -55,6 +61,8 @@ static_assert(kPagesPerTile * kBlockSize == kTileTok, "tiles are whole pages");
 static_assert(kTileTok * kHeadDim * 2 == kPfThreads * 4 * 16, "four 16-byte K loads per thread");
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -79,6 +87,56 @@ __device__ __forceinline__ int vt_offset(int d, int granule) {
 __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f4 mfma32(b8 a, b8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const h2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Operand type of the score product: bf16 for a bf16 cache, fp16 for every other format.
+// The P V product is fp16 for every format.
+template <KvType kKv> struct PfOperand { typedef h8 V8; };
+template <> struct PfOperand<KvType::kBF16> { typedef b8 V8; };
+
+// Two bf16 values (one dword, the lower one first) rounded to an fp16 pair.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xffff0000u));
+}
+
+
+// Eight stored 1-byte codes (lowest address first) times the row's scale, as eight fp16
+// values: INT8 codes exactly through fp32 (the sign bit flipped makes them unsigned bytes
+// u = x + 128, and x s = u s - 128 s in one fma), E4M3 codes exactly to fp16 by the hardware
+// conversion (unit scale), then times s in fp32; each product is rounded once to fp16.
+template <KvType kKv>
+__device__ __forceinline__ u32x4 dequant8(u32x2 w, float sc) {
+  u32x4 r;
+  if constexpr (kKv == KvType::kI8) {
+    const float bias = -128.0f * sc;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t u = w[h] ^ 0x80808080u;
+      const float x0 = __builtin_fmaf(static_cast<float>(u & 0xffu), sc, bias);
+      const float x1 = __builtin_fmaf(static_cast<float>((u >> 8) & 0xffu), sc, bias);
+      const float x2 = __builtin_fmaf(static_cast<float>((u >> 16) & 0xffu), sc, bias);
+      const float x3 = __builtin_fmaf(static_cast<float>(u >> 24), sc, bias);
+      r[2 * h] = pack_f16(x0, x1);
+      r[2 * h + 1] = pack_f16(x2, x3);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, false);
+      const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[h], 1.0f, true);
+      r[2 * h] = pack_f16(static_cast<float>(lo.x) * sc, static_cast<float>(lo.y) * sc);
+      r[2 * h + 1] = pack_f16(static_cast<float>(hi.x) * sc, static_cast<float>(hi.y) * sc);
+    }
+  }
+  return r;
+}
 
 // One workgroup: query-row block mb of (sequence b, KV head g), looping over further blocks
 // `nx` apart. The grid is one-dimensional, nx * Hkv * B workgroups. Work order: for batches
@@ -87,9 +145,13 @@ __device__ __forceinline__ f4 mfma32(h8 a, h8 b, f4 c) {
 // last rows first, since later rows see more of the cache. When the pair count is a
 // multiple of the die count, all row blocks of a pair run on one die, so its K/V pages are
 // fetched into that die's L2 once.
-template <int kGroup>
+template <KvType kKv, int kGroup>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a, int nx) {
+  constexpr bool kCodes = kv_scaled(kKv);                      // 1-byte codes + row scales
+  constexpr int kRowBytes = kHeadDim * kv_elem_bytes(kKv);     // one stored (token, head) row
+  constexpr int kPageB = kBlockSize * kRowBytes;               // one stored (page, head) tile
+  using V8 = typename PfOperand<kKv>::V8;
   __shared__ __attribute__((aligned(16))) unsigned char s_k[kTileTok * kKStride];
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[kHeadDim * kVtStride];
   __shared__ int s_len[kOrderMaxPf];
@@ -168,9 +230,10 @@ void prefill_kernel(PrefillArgs a, int nx) {
   const int st = tid >> 4;
   const int vs = lane & 3;
   const int vc = lane >> 2;
-  const char* kbase = static_cast<const char*>(a.k_pages) + static_cast<size_t>(g) * kPageBytes;
-  const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageBytes;
-  const size_t page_stride = static_cast<size_t>(a.n_kv_heads) * kPageBytes;
+  const char* kbase = static_cast<const char*>(a.k_pages) + static_cast<size_t>(g) * kPageB;
+  const char* vbase = static_cast<const char*>(a.v_pages) + static_cast<size_t>(g) * kPageB;
+  const size_t page_stride = static_cast<size_t>(a.n_kv_heads) * kPageB;
+  const size_t scale_stride = static_cast<size_t>(a.n_kv_heads) * kBlockSize;   // floats per page
 
   for (int mb = mbx; mb * kRowsPerBlock < rows_total; mb += nx) {
     const int wrow0 = mb * kRowsPerBlock + wave * kRowsPerWave;
@@ -178,7 +241,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
     // each group. Q^T as the B operand: Q[row][32 kb + 8 quad + e].
     // A negative scale is applied as |scale| to -q (exact), so that the largest score is the
     // largest product and the scale folds into one fma per score.
-    h8 qb[kRowGroups][4];
+    V8 qb[kRowGroups][4];
     int pos[kRowGroups];        // last visible token of the lane's row (-1: none)
     int diag_from[kRowGroups];  // last visible token of the group's first row
 #pragma unroll
@@ -190,15 +253,15 @@ void prefill_kernel(PrefillArgs a, int nx) {
       pos[grp] = live && !bad ? L - C + tok : -1;
       const int first = wrow0 + 16 * grp;
       diag_from[grp] = first < rows_total ? L - C + first / kGroup : INT_MAX;
-      const _Float16* qp = static_cast<const _Float16*>(a.q) +
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                            (static_cast<size_t>(r0 + tok) * hq + g * kGroup + h) * kHeadDim + 8 * quad;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         if (live) {
           const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 32 * kb);
-          qb[grp][kb] = __builtin_bit_cast(h8, w ^ qflip);
+          qb[grp][kb] = __builtin_bit_cast(V8, w ^ qflip);
         } else {
-          qb[grp][kb] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+          qb[grp][kb] = __builtin_bit_cast(V8, u32x4{0u, 0u, 0u, 0u});
         }
       }
     }
@@ -224,7 +287,11 @@ void prefill_kernel(PrefillArgs a, int nx) {
     // (its cache lines are fetched anyway): their slots may hold anything, NaN included.
     // Their scores are masked, and their V rows are staged as zeros, since a zero weight
     // times NaN would still be NaN in P V.
+    // 2-byte formats load straight into kr/vr; 1-byte formats load codes and row scales
+    // into kc/vcode/ksc/vsc, dequantised into kr/vr when the tile is staged.
     u32x4 kr[4], vr[4];
+    u32x2 kc[4], vcode[4];
+    float ksc[4], vsc[4];
     auto fetch = [&](int j) __attribute__((always_inline)) {
       const int last_slot = (L - 1) % kBlockSize;
       // Page ids of the tile's four pages: uniform, through the scalar cache.
@@ -234,26 +301,57 @@ void prefill_kernel(PrefillArgs a, int nx) {
 #pragma unroll
       for (int i = 0; i < kPagesPerTile; ++i) {
         const int t = (kPagesPerTile * j + i) * kBlockSize + st;
-        const uint32_t off = (t < L ? st : last_slot) * (kHeadDim * 2) + sc * 16;
-        kr[i] = *reinterpret_cast<const u32x4*>(kbase + phys[i] * page_stride + off);
+        const int slot = t < L ? st : last_slot;
+        const char* row = kbase + phys[i] * page_stride + slot * kRowBytes;
+        if constexpr (kCodes) {
+          kc[i] = *reinterpret_cast<const u32x2*>(row + sc * 8);
+          ksc[i] = a.k_scale[phys[i] * scale_stride + g * kBlockSize + slot];
+        } else {
+          kr[i] = *reinterpret_cast<const u32x4*>(row + sc * 16);
+        }
       }
       const int vphys = wave == 0 ? phys[0] : wave == 1 ? phys[1] : wave == 2 ? phys[2] : phys[3];
       const char* vpage = vbase + vphys * page_stride;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = kTileTok * j + kBlockSize * wave + 4 * vs + e;
-        const uint32_t off = (t < L ? 4 * vs + e : last_slot) * (kHeadDim * 2) + vc * 16;
-        vr[e] = *reinterpret_cast<const u32x4*>(vpage + off);
+        const int slot = t < L ? 4 * vs + e : last_slot;
+        if constexpr (kCodes) {
+          vcode[e] = *reinterpret_cast<const u32x2*>(vpage + slot * kRowBytes + vc * 8);
+          vsc[e] = a.v_scale[vphys * scale_stride + g * kBlockSize + slot];
+        } else {
+          vr[e] = *reinterpret_cast<const u32x4*>(vpage + slot * kRowBytes + vc * 16);
+        }
       }
       if (kTileTok * (j + 1) > L) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (kTileTok * j + kBlockSize * wave + 4 * vs + e >= L) vr[e] = u32x4{0u, 0u, 0u, 0u};
+        for (int e = 0; e < 4; ++e) {
+          if (kTileTok * j + kBlockSize * wave + 4 * vs + e >= L) {
+            if constexpr (kCodes) {
+              vcode[e] = u32x2{0u, 0u};
+            } else {
+              vr[e] = u32x4{0u, 0u, 0u, 0u};
+            }
+          }
+        }
       }
     };
     if (tiles > 0) fetch(0);
     for (int j = 0; j < tiles; ++j) {
       __syncthreads();   // the previous tile is no longer read
+      if constexpr (kCodes) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kr[i] = dequant8<kKv>(kc[i], ksc[i]);
+          vr[i] = dequant8<kKv>(vcode[i], vsc[i]);
+        }
+      } else if constexpr (kKv == KvType::kBF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) vr[i][x] = bf16x2_to_f16x2(vr[i][x]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4*>(s_k + (st + 16 * i) * kKStride + sc * 16) = kr[i];
@@ -284,7 +382,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
         s[1][sb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const h8 ka = __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(
+          const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
               s_k + (16 * sb + col) * kKStride + (32 * kb + 8 * quad) * 2));
           s[0][sb] = mfma32(ka, qb[0][kb], s[0][sb]);
           s[1][sb] = mfma32(ka, qb[1][kb], s[1][sb]);
@@ -375,9 +473,21 @@ void prefill_kernel(PrefillArgs a, int nx) {
   }
 }
 
+template <KvType kKv>
+hipError_t launch_prefill_kv(int group, const PrefillArgs& a, dim3 grid, int nx, hipStream_t stream) {
+  switch (group) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<kKv, 1>), grid, dim3(kPfThreads), 0, stream, a, nx); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<kKv, 2>), grid, dim3(kPfThreads), 0, stream, a, nx); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<kKv, 4>), grid, dim3(kPfThreads), 0, stream, a, nx); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<kKv, 8>), grid, dim3(kPfThreads), 0, stream, a, nx); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_prefill(int group, const PrefillArgs& a, int max_chunk, hipStream_t stream) {
+hipError_t launch_prefill(KvType kv, int group, const PrefillArgs& a, int max_chunk, hipStream_t stream) {
   // nx row blocks per (sequence, KV head); workgroups loop over the rest of a longer chunk.
   // The grid stays below 2^24 workgroups (2^32 work-items).
   const long long pairs = static_cast<long long>(a.batch) * a.n_kv_heads;
@@ -387,14 +497,13 @@ hipError_t launch_prefill(int group, const PrefillArgs& a, int max_chunk, hipStr
   if (nx < 1) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(nx * pairs));
   const int nxi = static_cast<int>(nx);
-  switch (group) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(kPfThreads), 0, stream, a, nxi); break;
-    default: return hipErrorInvalidValue;
+  switch (kv) {
+    case KvType::kF16: return launch_prefill_kv<KvType::kF16>(group, a, grid, nxi, stream);
+    case KvType::kBF16: return launch_prefill_kv<KvType::kBF16>(group, a, grid, nxi, stream);
+    case KvType::kI8: return launch_prefill_kv<KvType::kI8>(group, a, grid, nxi, stream);
+    case KvType::kFP8: return launch_prefill_kv<KvType::kFP8>(group, a, grid, nxi, stream);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dattn

@@ -169,15 +169,16 @@ def _poison_unused_slots(w: Workload, n_used_pages: int) -> None:
 
 def prefill_rows(w: "Workload", chunk: Optional[int] = None, seed: Optional[int] = None):
     """Chunk query rows for a prefill step over workload w: C_b = min(chunk, L_b) rows per
-    sequence, stacked in sequence order. Returns (q [T, Hq, D] fp16 ~ N(0, 1), q_start
-    int32 [B + 1]). Drawn from their own stream (seed + 1), so w's draws are unchanged."""
+    sequence, stacked in sequence order. Returns (q [T, Hq, D] ~ N(0, 1), fp16, or bf16 bit
+    patterns (uint16) for a bf16 cache, and q_start int32 [B + 1]). Drawn from their own
+    stream (seed + 1), so w's draws are unchanged."""
     c = w.config
     chunk = c.chunk if chunk is None else int(chunk)
     sizes = np.minimum(np.asarray(w.seq_lens, dtype=np.int64), chunk)
     q_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     rng = np.random.default_rng((w.seed if seed is None else int(seed)) + 1)
-    q = rng.standard_normal((int(q_start[-1]), c.n_q_heads, c.head_dim),
-                            dtype=np.float32).astype(np.float16)
+    q32 = rng.standard_normal((int(q_start[-1]), c.n_q_heads, c.head_dim), dtype=np.float32)
+    q = _bf16_bits(q32) if c.kv_dtype == "bf16" else q32.astype(np.float16)
     return q, q_start
 
 

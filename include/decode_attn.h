@@ -239,35 +239,41 @@ int decode_attn_append(const void* k_new, const void* v_new, const int32_t* bloc
  * with g = h / G. A decode token is a chunk of one, so prefill chunks and decode tokens can
  * share a call.
  *
- *     q         fp16 [total_rows, n_q_heads, head_dim], 16-byte aligned: all chunks' rows
+ *     q         [total_rows, n_q_heads, head_dim], 16-byte aligned: all chunks' rows; fp16,
+ *               or bf16 for a BF16 cache (as for decode_attn)
  *     q_start   int32 [batch + 1]: 0 <= q_start[b] <= q_start[b+1] <= total_rows
- *     k_pages, v_pages, block_table, seq_lens, num_pages: as for decode_attn (fp16 pools)
+ *     k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, num_pages, kv_dtype: as for
+ *               decode_attn (row scales present iff INT8 or FP8)
  *     max_chunk an upper bound on C_b, used only to size the grid (total_rows is always
  *               safe); longer chunks are still computed in full
  *     out       fp32 [total_rows, n_q_heads, head_dim], 16-byte aligned; rows outside every
  *               chunk are not written
  *
- * Both products run on the matrix cores (fp16 inputs, fp32 accumulation), with the softmax
- * weights rounded to fp16 for the second one. Bad device values never fault: a sequence
- * whose q_start range leaves [0, total_rows] or is empty is skipped; one whose chunk is
- * longer than L_b, whose L_b exceeds the table, or whose table holds a page id outside
- * [0, num_pages) among its first ceil(L_b / block_size) entries gets NaN in all its rows.
- * Supported: kv_dtype FP16 (others return DECODE_ATTN_ERR_UNSUPPORTED), head_dim 128,
- * block_size 16, G in {1, 2, 4, 8}, batch * n_kv_heads below 2^24. Asynchronous on
- * `stream`; never allocates; capturable in a HIP graph. Returns a decode_attn_status.
+ * Both products run on the matrix cores with fp32 accumulation. The scores take fp16 q and
+ * K (bf16 for a BF16 cache); the weighted sum of V takes the softmax weights rounded to fp16
+ * and V as fp16. BF16 V rows are rounded to fp16 on the way in, and INT8 and FP8 rows are
+ * dequantised on the way in (code times the row's scale, rounded once to fp16), so those
+ * values must lie within fp16's range (|value| < 65504); values below fp16's normal range
+ * (2^-14) keep fp16's subnormal precision. Bad device values never
+ * fault: a sequence whose q_start range leaves [0, total_rows] or is empty is skipped; one
+ * whose chunk is longer than L_b, whose L_b exceeds the table, or whose table holds a page
+ * id outside [0, num_pages) among its first ceil(L_b / block_size) entries gets NaN in all
+ * its rows. Supported: head_dim 128, block_size 16, G in {1, 2, 4, 8}, batch * n_kv_heads
+ * below 2^24. Asynchronous on `stream`; never allocates; capturable in a HIP graph. Returns
+ * a decode_attn_status.
  */
 int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pages,
-                        const void* v_pages, const int32_t* block_table,
-                        const int32_t* seq_lens, int batch, int total_rows,
-                        int max_blocks_per_seq, int num_pages, int n_q_heads, int n_kv_heads,
-                        int head_dim, int block_size, int kv_dtype, int max_chunk, float scale,
-                        float* out, hipStream_t stream);
+                        const void* v_pages, const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens, int batch,
+                        int total_rows, int max_blocks_per_seq, int num_pages, int n_q_heads,
+                        int n_kv_heads, int head_dim, int block_size, int kv_dtype, int max_chunk,
+                        float scale, float* out, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);
 
 /* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats;
-   6.1 adds decode_attn_prefill. */
+   6.1 adds decode_attn_prefill; 6.2 gives it every storage format (row scale arguments). */
 int decode_attn_version(void);
 
 #ifdef __cplusplus

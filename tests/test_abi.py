@@ -51,7 +51,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 1
+    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 2
     names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -271,23 +271,27 @@ def test_append_host_validation(lib, over, status):
 
 # decode_attn_prefill: fake device addresses; every case fails host-side validation (or
 # enqueues nothing).
-PREFILL = dict(q=A, qs=2 * A, k=3 * A, v=4 * A, bt=5 * A, sl=6 * A, batch=2, total=10, mb=8,
-               np_=16, hq=8, hkv=2, d=128, bs=16, kv=0, chunk=8, scale=0.088, out=7 * A)
+PREFILL = dict(q=A, qs=2 * A, k=3 * A, v=4 * A, ks=None, vs=None, bt=5 * A, sl=6 * A, batch=2,
+               total=10, mb=8, np_=16, hq=8, hkv=2, d=128, bs=16, kv=0, chunk=8, scale=0.088,
+               out=7 * A)
 
 
 def call_prefill(lib, **over):
     a = dict(PREFILL, **over)
-    return lib.decode_attn_prefill(a["q"], a["qs"], a["k"], a["v"], a["bt"], a["sl"], a["batch"],
-                                   a["total"], a["mb"], a["np_"], a["hq"], a["hkv"], a["d"],
-                                   a["bs"], a["kv"], a["chunk"], a["scale"], a["out"], None)
+    return lib.decode_attn_prefill(a["q"], a["qs"], a["k"], a["v"], a["ks"], a["vs"], a["bt"],
+                                   a["sl"], a["batch"], a["total"], a["mb"], a["np_"], a["hq"],
+                                   a["hkv"], a["d"], a["bs"], a["kv"], a["chunk"], a["scale"],
+                                   a["out"], None)
 
 
 @pytest.mark.parametrize("over,status", [
     (dict(hq=6, hkv=4), 1),                  # Hq % Hkv != 0
     (dict(hq=6, hkv=2), 2),                  # G = 3
-    (dict(kv=1), 2),                         # int8 pools: not supported by the prefill
-    (dict(kv=2), 2),                         # bf16
-    (dict(kv=3), 2),                         # fp8
+    (dict(kv=1), 1),                         # int8 pools without row scales
+    (dict(kv=3, ks=8 * A), 1),               # fp8 with only one of the two scale arrays
+    (dict(kv=2, ks=8 * A, vs=9 * A), 1),     # bf16 pools with row scales
+    (dict(kv=0, vs=9 * A), 1),               # fp16 pools with a row scale
+    (dict(kv=1, ks=8 * A + 2, vs=9 * A), 1), # row scales not 4-byte aligned
     (dict(kv=7), 1),                         # unknown storage type
     (dict(d=64), 2),
     (dict(bs=8), 2),

@@ -41,32 +41,43 @@ def chunk_layout(lens, rng, kinds=("full", "one", "rand")):
     return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
 
 
+def draw_q(rng, rows, cfg):
+    """Chunk rows ~ N(0, 1): fp16, or bf16 bit patterns (uint16) for a bf16 cache."""
+    q32 = rng.standard_normal((rows, cfg.n_q_heads, 128)).astype(np.float32)
+    if cfg.kv_dtype == "bf16":
+        return (q32.view(np.uint32) >> 16).astype(np.uint16)
+    return q32.astype(np.float16)
+
+
 def run(torch, lib, w, q, q_start, max_chunk=None, out=None):
     t = lambda a: dev_tensor(torch, a)
     got = lib.decode_attn_prefill(t(q), t(q_start), t(w.k_pages), t(w.v_pages), t(w.block_table),
-                                  t(w.seq_lens), w.scale, max_chunk=max_chunk, out=out)
+                                  t(w.seq_lens), w.scale, k_scale=t(w.k_scale),
+                                  v_scale=t(w.v_scale), max_chunk=max_chunk, out=out)
     torch.cuda.synchronize()
     return got.cpu().numpy()
 
 
 def reference(w, q, q_start):
     return oracle.prefill_attention(q, w.k_pages, w.v_pages, w.block_table, w.seq_lens,
-                                    q_start, w.scale)[0]
+                                    q_start, w.scale, w.k_scale, w.v_scale)[0]
 
 
+@pytest.mark.parametrize("kv", ["fp16", "bf16", "int8", "fp8"])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("seed", [1, 2])
-def test_small_mixed_chunks(torch, lib, group, seed):
-    cfg = SMALL.with_(n_q_heads=2 * group, n_kv_heads=2)
+def test_small_mixed_chunks(torch, lib, kv, group, seed):
+    # NaN canaries sit in every slot no token owns, scales included.
+    cfg = SMALL.with_(n_q_heads=2 * group, n_kv_heads=2, kv_dtype=kv)
     w = generate(cfg, seed=200 + seed, poison=True, extra_pages=3)
     rng = np.random.default_rng(seed)
     q_start = chunk_layout(w.seq_lens, rng)
-    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, 128)).astype(np.float16)
-    print(f"case prefill G={group} seed={seed} lens={w.seq_lens.tolist()} "
+    q = draw_q(rng, int(q_start[-1]), cfg)
+    print(f"case prefill {kv} G={group} seed={seed} lens={w.seq_lens.tolist()} "
           f"chunks={np.diff(q_start).tolist()}", flush=True)
     got = run(torch, lib, w, q, q_start)
     assert np.isfinite(got).all(), "a NaN canary leaked"
-    assert_parity(got, reference(w, q, q_start), f"prefill G={group}")
+    assert_parity(got, reference(w, q, q_start), f"prefill {kv} G={group}")
 
 
 @pytest.mark.parametrize("max_chunk", [1, 7, 64, 10000])
@@ -234,3 +245,37 @@ def test_deterministic(torch, lib):
     first = run(torch, lib, w, q, q_start)
     second = run(torch, lib, w, q, q_start)
     assert np.array_equal(first, second)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_formats_at_the_preset_shape(torch, lib, kv):
+    """The prefill preset's shapes over the other storage formats, in the launch the
+    benchmark times, on its shortest sequence."""
+    cfg = CONFIGS[8].with_(kv_dtype=kv)
+    w = generate(cfg)
+    q, q_start = prefill_rows(w)
+    print(f"case prefill preset {kv} rows={q.shape[0]}", flush=True)
+    got = run(torch, lib, w, q, q_start, max_chunk=cfg.chunk)
+    assert np.isfinite(got).all()
+    b = int(np.argmin(w.seq_lens))
+    rows = slice(int(q_start[b]), int(q_start[b + 1]))
+    sub_start = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
+    ref = oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
+                                   w.seq_lens[b:b + 1], sub_start, w.scale,
+                                   None if w.k_scale is None else w.k_scale,
+                                   None if w.v_scale is None else w.v_scale)[0]
+    assert_parity(got[rows], ref, f"preset {kv} sequence {b}")
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+def test_coded_one_token_chunks_match_decode(torch, lib, kv):
+    # One-token chunks over a coded cache: the prefill (dequantised on staging, fp16 matrix
+    # cores) and decode (codes in registers, scales on scores and weights) both within the
+    # tolerance of the oracle.
+    cfg = SMALL.with_(kv_dtype=kv)
+    w = generate(cfg, seed=306)
+    q_start = np.arange(cfg.batch + 1, dtype=np.int32)
+    got = run(torch, lib, w, w.q, q_start)
+    ref = oracle.decode_attention(w.q, w.k_pages, w.v_pages, w.block_table, w.seq_lens, w.scale,
+                                  w.k_scale, w.v_scale)[0]
+    assert_parity(got, ref, f"{kv} one-token chunks")
