@@ -302,12 +302,16 @@ void prefill_kernel(PrefillArgs a, int nx) {
       for (int i = 0; i < kPagesPerTile; ++i) {
         const int t = (kPagesPerTile * j + i) * kBlockSize + st;
         const int slot = t < L ? st : last_slot;
-        const char* row = kbase + phys[i] * page_stride + slot * kRowBytes;
+        // SGPR page base plus an unsigned 32-bit lane offset (the scalar-base load form).
+        const char* page = kbase + phys[i] * page_stride;
         if constexpr (kCodes) {
-          kc[i] = *reinterpret_cast<const u32x2*>(row + sc * 8);
-          ksc[i] = a.k_scale[phys[i] * scale_stride + g * kBlockSize + slot];
+          const uint32_t off = static_cast<uint32_t>(slot * kRowBytes + sc * 8);
+          kc[i] = *reinterpret_cast<const u32x2*>(page + off);
+          const float* srow = a.k_scale + phys[i] * scale_stride + g * kBlockSize;   // uniform
+          ksc[i] = srow[static_cast<uint32_t>(slot)];
         } else {
-          kr[i] = *reinterpret_cast<const u32x4*>(row + sc * 16);
+          const uint32_t off = static_cast<uint32_t>(slot * kRowBytes + sc * 16);
+          kr[i] = *reinterpret_cast<const u32x4*>(page + off);
         }
       }
       const int vphys = wave == 0 ? phys[0] : wave == 1 ? phys[1] : wave == 2 ? phys[2] : phys[3];
@@ -317,10 +321,13 @@ void prefill_kernel(PrefillArgs a, int nx) {
         const int t = kTileTok * j + kBlockSize * wave + 4 * vs + e;
         const int slot = t < L ? 4 * vs + e : last_slot;
         if constexpr (kCodes) {
-          vcode[e] = *reinterpret_cast<const u32x2*>(vpage + slot * kRowBytes + vc * 8);
-          vsc[e] = a.v_scale[vphys * scale_stride + g * kBlockSize + slot];
+          const uint32_t off = static_cast<uint32_t>(slot * kRowBytes + vc * 8);
+          vcode[e] = *reinterpret_cast<const u32x2*>(vpage + off);
+          const float* srow = a.v_scale + vphys * scale_stride + g * kBlockSize;    // uniform per wave
+          vsc[e] = srow[static_cast<uint32_t>(slot)];
         } else {
-          vr[e] = *reinterpret_cast<const u32x4*>(vpage + slot * kRowBytes + vc * 16);
+          const uint32_t off = static_cast<uint32_t>(slot * kRowBytes + vc * 16);
+          vr[e] = *reinterpret_cast<const u32x4*>(vpage + off);
         }
       }
       if (kTileTok * (j + 1) > L) {
