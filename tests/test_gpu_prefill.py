@@ -279,3 +279,21 @@ def test_coded_one_token_chunks_match_decode(torch, lib, kv):
     ref = oracle.decode_attention(w.q, w.k_pages, w.v_pages, w.block_table, w.seq_lens, w.scale,
                                   w.k_scale, w.v_scale)[0]
     assert_parity(got, ref, f"{kv} one-token chunks")
+
+
+def test_empty_chunks_and_empty_sequences(torch, lib):
+    # Sequences with no chunk rows (C_b = 0, some of them with L_b = 0 too) sit between real
+    # chunks: they write nothing and leave the other sequences' rows exact.
+    cfg = SMALL.with_(batch=6, len_lo=1, len_hi=120)
+    lens = np.array([0, 57, 33, 0, 120, 9], dtype=np.int32)
+    w = generate(cfg, seed=307, poison=True, seq_lens=lens)
+    sizes = np.array([0, 57, 0, 0, 40, 9])
+    q_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rng = np.random.default_rng(307)
+    q = draw_q(rng, int(q_start[-1]), cfg)
+    print("case prefill empty chunks", flush=True)
+    t = lambda a: dev_tensor(torch, a)
+    out = torch.full(q.shape, 777.0, dtype=torch.float32, device="cuda:0")
+    got = run(torch, lib, w, q, q_start, out=out)
+    assert np.isfinite(got).all()
+    assert_parity(got, reference(w, q, q_start), "empty chunks")
