@@ -221,3 +221,39 @@ def test_planted_short_mask_fails_a_pin(monkeypatch):
 def test_planted_mistakes_fail_a_pin(monkeypatch, name):
     monkeypatch.setattr(oracle, "prefill_attention", MUTANTS[name])
     assert not pins_pass(), f"planted mistake not caught: {name}"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+def test_one_token_chunks_are_decode_attention_in_every_format(kv):
+    # The prefill and decode oracles decode the stored formats through the same pinned
+    # routines; one-token chunks must give the decode result bit for bit in each format.
+    cfg = TINY.with_(kv_dtype=kv)
+    w = generate(cfg, seed=8)
+    q_start = np.arange(cfg.batch + 1, dtype=np.int32)
+    out, lse = run(w, w.q, q_start, out_dtype=np.float64)
+    want, want_lse = oracle.decode_attention(w.q, w.k_pages, w.v_pages, w.block_table,
+                                             w.seq_lens, w.scale, w.k_scale, w.v_scale,
+                                             out_dtype=np.float64)
+    assert np.array_equal(out, want) and np.array_equal(lse, want_lse)
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+def test_coded_rows_equal_their_dequantised_values(kv):
+    # A coded cache with row scales gives the prefill result of a float64 cache holding
+    # code x scale, row by row: pins that each row takes its own scale, K's for K and V's
+    # for V.
+    cfg = TINY.with_(kv_dtype=kv)
+    w, _, q_start = chunked(cfg, 9)
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((int(q_start[-1]), cfg.n_q_heads, cfg.head_dim)).astype(np.float16)
+    out, lse = run(w, q, q_start, out_dtype=np.float64)
+    kd = oracle.element_values(w.k_pages) * w.k_scale[..., None].astype(np.float64)
+    vd = oracle.element_values(w.v_pages) * w.v_scale[..., None].astype(np.float64)
+    want, want_lse = oracle.prefill_attention(q, kd, vd, w.block_table, w.seq_lens, q_start,
+                                              w.scale, out_dtype=np.float64)
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-13, atol=1e-15)
+    swapped, _ = oracle.prefill_attention(q, w.k_pages, w.v_pages, w.block_table, w.seq_lens,
+                                          q_start, w.scale, w.v_scale, w.k_scale,
+                                          out_dtype=np.float64)
+    assert not np.allclose(swapped, want, rtol=1e-6, atol=1e-9)
