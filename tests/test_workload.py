@@ -6,7 +6,8 @@ import os
 import numpy as np
 import pytest
 
-from decode_phase_attention_paged_amd.workload import CONFIGS, Config, generate, kv_read_bytes
+from decode_phase_attention_paged_amd.workload import (CONFIGS, Config, generate, kv_read_bytes,
+                                                     prefill_flops, prefill_rows)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -111,3 +112,30 @@ def test_bf16_and_fp8_presets_draw_the_stated_values():
     assert wf.k_scale.min() >= 0.005 * 127 / 448 * 0.999 and wf.k_scale.max() <= 0.02 * 127 / 448
     assert wf.kv_bytes == int(wf.seq_lens.sum()) * 32 * 2 * (128 + 4)
     assert wb.kv_bytes == int(wb.seq_lens.sum()) * 32 * 2 * 256
+
+
+def test_prefill_flops_count_every_visible_pair():
+    # Brute force: every (chunk row, visible token) pair costs 4 D flops per query head.
+    lens = np.array([5, 1, 9, 16], dtype=np.int32)
+    q_start = np.array([0, 3, 4, 13, 13], dtype=np.int32)      # chunks 3, 1, 9, 0
+    pairs = 0
+    for b, n in enumerate(lens):
+        c = int(q_start[b + 1] - q_start[b])
+        for i in range(c):
+            pairs += sum(1 for t in range(n) if t <= n - c + i)
+    assert prefill_flops(lens, q_start, 6, 8) == pairs * 6 * 4 * 8
+
+
+def test_prefill_rows_layout_and_formats():
+    w = generate(CONFIGS[8].with_(batch=3, len_lo=20, len_hi=900))
+    q, q_start = prefill_rows(w)
+    assert q.dtype == np.float16 and q_start.dtype == np.int32
+    np.testing.assert_array_equal(np.diff(q_start), np.minimum(w.seq_lens, 512))
+    assert q.shape == (int(q_start[-1]), 32, 128)
+    wb = generate(CONFIGS[8].with_(batch=3, len_lo=20, len_hi=900, kv_dtype="bf16"))
+    qb, _ = prefill_rows(wb)
+    assert qb.dtype == np.uint16                     # bf16 bit patterns for a bf16 cache
+    # Drawn from their own stream: the workload's arrays are the same with or without them.
+    w2 = generate(CONFIGS[8].with_(batch=3, len_lo=20, len_hi=900))
+    np.testing.assert_array_equal(w.k_pages, w2.k_pages)
+    np.testing.assert_array_equal(q, prefill_rows(w2)[0])
