@@ -175,6 +175,8 @@ def main():
                          "chunked-prefill attention (default workload: the prefill preset)")
     args = ap.parse_args()
 
+    if args.kv is not None and args.op != "prefill":
+        ap.error("--kv applies to --op prefill only; the decode presets fix their formats")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this library runs decode attention on a single "
