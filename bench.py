@@ -514,7 +514,12 @@ def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
         seqs += 1
         if spent >= budget_s:
             break
-    return {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{seqs} of {c.batch} sequences, shortest first ({spent:.1f} s)"}
 
