@@ -297,3 +297,27 @@ def test_empty_chunks_and_empty_sequences(torch, lib):
     got = run(torch, lib, w, q, q_start, out=out)
     assert np.isfinite(got).all()
     assert_parity(got, reference(w, q, q_start), "empty chunks")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_random_shapes(torch, lib, case):
+    # Seeded draws over formats, group sizes, batch sizes, lengths and chunk layouts
+    # (including chunks longer than one workgroup's 128 rows and grids sized below them).
+    rng = np.random.default_rng(400 + case)
+    kv = ["fp16", "bf16", "int8", "fp8"][case % 4]
+    group = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.integers(1, 4))
+    batch = int(rng.integers(1, 7))
+    hi = int(rng.integers(16, 400))
+    cfg = SMALL.with_(batch=batch, n_q_heads=group * hkv, n_kv_heads=hkv, len_lo=1, len_hi=hi,
+                      kv_dtype=kv, scale=float(rng.uniform(0.02, 0.2)))
+    w = generate(cfg, seed=500 + case, poison=True, extra_pages=int(rng.integers(0, 3)))
+    sizes = np.array([int(rng.integers(0, n + 1)) for n in w.seq_lens])
+    q_start = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    q = draw_q(rng, int(q_start[-1]), cfg)
+    max_chunk = int(rng.choice([1, 16, max(1, int(sizes.max()))]))
+    print(f"case prefill random {case}: {kv} G={group} Hkv={hkv} lens={w.seq_lens.tolist()} "
+          f"chunks={sizes.tolist()} max_chunk={max_chunk}", flush=True)
+    got = run(torch, lib, w, q, q_start, max_chunk=max_chunk)
+    assert np.isfinite(got).all(), "a NaN canary leaked"
+    assert_parity(got, reference(w, q, q_start), f"random case {case}")
