@@ -169,7 +169,7 @@ def main():
                          "replays of it (the step count is rounded up to a multiple)")
     ap.add_argument("--kv", choices=["fp16", "bf16", "int8", "fp8"], default=None,
                     help="prefill only: run the preset's shapes over another storage format")
-    ap.add_argument("--op", choices=["attn", "append", "prefill"], default="attn",
+    ap.add_argument("--op", choices=["attn", "append", "prefill", "step"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
                          "that precedes it in a decode step, on the same workload; prefill: "
                          "chunked-prefill attention (default workload: the prefill preset)")
@@ -201,6 +201,8 @@ def main():
         return bench_append(args, cfg, lib, torch, np, binding, generate)
     if args.op == "prefill":
         return bench_prefill(args, cfg, lib, torch, np, binding, generate)
+    if args.op == "step":
+        return bench_step(args, cfg, lib, torch, np, binding, generate)
     log(f"generating {cfg.name} ...")
     w = generate(cfg)
     dev = torch.device("cuda:0")
@@ -494,6 +496,111 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
     }
     print(json.dumps(record), flush=True)
 
+
+
+def bench_step(args, cfg, lib, torch, np, binding, generate):
+    """Time a whole decode step: decode_attn_append writes every sequence's new K/V row at
+    position L_b (a fresh page where the token starts one), then decode_attn attends over
+    the grown caches (L_b + 1 tokens), with the library's own plan. Two launches per step;
+    the pools rotate over replicas as for the attention alone."""
+    from decode_phase_attention_paged_amd.workload import ELEM_BYTES, SCALE_BYTES, kv_read_bytes
+    log(f"generating {cfg.name} for a decode step ...")
+    w = generate(cfg)
+    table = w.block_table.copy()
+    positions = w.seq_lens.astype(np.int32).copy()
+    fresh = 0
+    for b in range(cfg.batch):
+        j = int(positions[b]) // cfg.block_size
+        if j >= table.shape[1]:
+            positions[b] = int(positions[b]) - 1      # a full table: rewrite the last slot
+        elif table[b, j] < 0:
+            table[b, j] = w.num_pages + fresh
+            fresh += 1
+    lens = (positions + 1).astype(np.int32)
+    n_pages = w.num_pages + fresh
+    grow = lambda a: None if a is None else np.concatenate(
+        [a, np.zeros((fresh,) + a.shape[1:], dtype=a.dtype)])
+    k_host, v_host, ks_host, vs_host = (grow(a) for a in (w.k_pages, w.v_pages, w.k_scale,
+                                                          w.v_scale))
+    rng = np.random.default_rng(w.seed + 1)
+    shape = (cfg.batch, cfg.n_kv_heads, cfg.head_dim)
+    new = [rng.standard_normal(shape, dtype=np.float32) for _ in range(2)]
+    new = [(x.view(np.uint32) >> 16).astype(np.uint16) if cfg.kv_dtype == "bf16"
+           else x.astype(np.float16) for x in new]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = lambda a: device_tensor(torch, np, a, dev)
+    q, bt, pos, sl, kn, vn = (t(a) for a in (w.q, table, positions, lens, new[0], new[1]))
+    pool_bytes = 2 * k_host.nbytes + (2 * ks_host.nbytes if ks_host is not None else 0)
+    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    pools = [(t(k_host), t(v_host), t(ks_host), t(vs_host)) for _ in range(reps)]
+    out = torch.empty(w.q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s_handle = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
+    kv_type = binding._KV_CODES[cfg.kv_dtype]
+    append_args, attn_args = [], []
+    for kp, vp, ks, vs in pools:
+        append_args.append((p(kn), p(vn), p(bt), p(pos), cfg.batch, cfg.max_blocks_per_seq,
+                            n_pages, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, kv_type,
+                            p(kp), p(vp), p(ks), p(vs), s_handle))
+        attn_args.append((p(q), p(kp), p(vp), p(ks), p(vs), p(bt), p(sl), cfg.batch,
+                          cfg.max_blocks_per_seq, n_pages, cfg.n_q_heads, cfg.n_kv_heads,
+                          cfg.head_dim, cfg.block_size, kv_type, float(w.scale), p(out),
+                          s_handle))
+
+    def step(i):
+        st = lib.decode_attn_append(*append_args[i % reps])
+        if st == 0:
+            st = lib.decode_attn(*attn_args[i % reps])
+        if st != 0:
+            raise RuntimeError(f"decode step failed: {binding.STATUS.get(st, st)}")
+
+    kv_bytes = kv_read_bytes(lens, cfg.n_kv_heads, cfg.head_dim, ELEM_BYTES[cfg.kv_dtype],
+                             SCALE_BYTES[cfg.kv_dtype])
+    nbytes = kv_bytes + append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.kv_dtype)
+    log(f"step: fresh_pages={fresh} replicas={reps} bytes/step={nbytes}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    start_ev.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    stop_ev.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start_ev.elapsed_time(stop_ev)
+    ms_per_step = total_ms / args.steps
+    gbs = nbytes * args.steps / (total_ms / 1e3) / 1e9
+    log(f"steps={args.steps} us/step={ms_per_step * 1e3:.2f} GB/s={gbs:.1f}")
+    record = {
+        "metric": "decode step (K/V append + attention) GB/s (fraction of MI355X HBM peak) + µs/step",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAMES[cfg.kv_dtype],
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "_step", "batch": cfg.batch,
+                   "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
+                   "head_dim": cfg.head_dim, "block_size": cfg.block_size,
+                   "kv_dtype": cfg.kv_dtype, "fresh_pages": fresh, "replicas": reps,
+                   "bytes_per_step": int(nbytes)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "append_kernel + attention (two launches)",
+                     "avg_launch_us": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(record), flush=True)
 
 def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
     """oracle.prefill_attention as it stands, timed on the host over whole sequences."""
