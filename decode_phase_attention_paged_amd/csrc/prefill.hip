@@ -452,11 +452,12 @@ void prefill_kernel(PrefillArgs a, int nx) {
         }
         l[grp] += sum;
       }
-      // O^T += V^T P^T over the tile's two 32-token halves.
+      // O^T += V^T P^T over the tile's two 32-token halves, half-major: consecutive
+      // products update different accumulators.
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int db = 0; db < 8; ++db) {
           const int d = 16 * db + col;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + quad));
           const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + 4 + quad));
