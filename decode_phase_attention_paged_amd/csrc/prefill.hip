@@ -388,19 +388,34 @@ void prefill_kernel(PrefillArgs a, int nx) {
         s[0][sb] = f4{0.f, 0.f, 0.f, 0.f};
         s[1][sb] = f4{0.f, 0.f, 0.f, 0.f};
       }
-      // d-slice major: the four subtiles' operands of one 32-wide d slice are read together
-      // and feed eight independent products.
+      if constexpr (!kCodes) {
+        // d-slice major: the four subtiles' operands of one 32-wide d slice are read together
+        // and feed eight independent products.
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        V8 ka[4];
+        for (int kb = 0; kb < 4; ++kb) {
+          V8 ka[4];
 #pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-          ka[sb] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
-              s_k + (16 * sb + col) * kKStride + (32 * kb + 8 * quad) * 2));
+          for (int sb = 0; sb < 4; ++sb)
+            ka[sb] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
+                s_k + (16 * sb + col) * kKStride + (32 * kb + 8 * quad) * 2));
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb) {
+            s[0][sb] = mfma32(ka[sb], qb[0][kb], s[0][sb]);
+            s[1][sb] = mfma32(ka[sb], qb[1][kb], s[1][sb]);
+          }
+        }
+      } else {
+        // Subtile major, one operand live at a time: the 1-byte formats keep their codes
+        // and row scales in registers too, and four live operands would spill.
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) {
-          s[0][sb] = mfma32(ka[sb], qb[0][kb], s[0][sb]);
-          s[1][sb] = mfma32(ka[sb], qb[1][kb], s[1][sb]);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const V8 ka = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(
+                s_k + (16 * sb + col) * kKStride + (32 * kb + 8 * quad) * 2));
+            s[0][sb] = mfma32(ka, qb[0][kb], s[0][sb]);
+            s[1][sb] = mfma32(ka, qb[1][kb], s[1][sb]);
+          }
         }
       }
       // Online softmax per row: lane holds S[row col][tile token 16 sb + 4 quad + e]. Only
