@@ -90,7 +90,9 @@ constexpr int kStreamWavesI8[4] = {2, 2, 1, 1};
 // Split mode runs a few long partitions per sequence, about one workgroup per CU, so each
 // wave keeps many tiles in flight.
 constexpr int kSplitDepthF16[4] = {4, 4, 3, 2};
-constexpr int kSplitDepthI8[4] = {6, 4, 3, 2};
+// 1-byte formats with G = 8: one unit in flight; at two the build spilled about 660 bytes
+// per lane to scratch and ran three times slower.
+constexpr int kSplitDepthI8[4] = {6, 4, 3, 1};
 constexpr int kSplitWavesF16[4] = {1, 1, 1, 1};
 constexpr int kSplitWavesI8[4] = {1, 1, 1, 1};
 // Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
