@@ -1,27 +1,40 @@
 #!/usr/bin/env python3
 """Decode-phase paged attention on one MI355X: KV-read GB/s and us/step.
 
-One step is one decode_attn call over the whole batch (the streaming kernel and
-the merge of the (sequence, head) pairs it cut): one layer's decode attention. The default workload is the Llama-2-7B-shaped MHA batch (batch 48,
-32 query = 32 KV heads, head_dim 128, seq_lens uniform in [18, 563], 16-token
-pages in a shuffled pool, fp16 K/V ~ N(0, 1)); --config picks another preset.
+One step is one decode_attn call over the whole batch: one layer's decode attention
+(the main kernel, plus the merge kernel when the plan cuts segments). The default
+workload is the largest single-GPU preset, the Llama-3-8B-shaped GQA batch: batch 160,
+32 query heads over 8 KV heads (group 4), head_dim 128, seq_lens uniform in [64, 4096],
+16-token pages in a shuffled pool, fp16 K/V ~ N(0, 1). --config picks another preset.
 
-Inputs are resident in HBM before timing starts. To keep the 256 MB Infinity
-Cache from serving the KV reads, the step rotates over R replicas of the page
-pools totalling at least 1 GiB. Throughput counts algorithmic KV bytes only:
-sum_b L_b * Hkv * 2 * D * elem (plus the fp32 row scales for INT8).
+Inputs are resident in HBM before timing starts. To keep the 256 MB Infinity Cache from
+serving the KV reads, the step rotates over R replicas of the page pools totalling at
+least 1 GiB. Throughput counts algorithmic KV bytes only: sum_b L_b * Hkv * 2 * D * elem
+(plus the fp32 row scales for INT8 and FP8).
+
+Timing: W warm-up steps, then `repeats` windows of exactly --steps back-to-back steps,
+each between one pair of HIP events on the launch stream with a device synchronisation
+on both sides. `value` and `us_per_step` are the median window; the spread is reported.
 
 Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py --summarize-profile DIR --tag TAG
+
+turns the rocprofv3 CSVs of one profiled workload (kernel trace, FETCH_SIZE, WRITE_SIZE
+and the counter passes, in the directory layout the summary lists) into
+profiles/<op>_<workload>.txt.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
 import ctypes
 import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -30,8 +43,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
 METRIC = "decode-attn KV-read GB/s (fraction of MI355X HBM peak) + µs/step"
 PROFILES = os.path.join(ROOT, "profiles")
+DEFAULT_CONFIG = {"attn": 3, "append": 2, "step": 2, "prefill": 8}
 
 
 def log(msg):
@@ -41,7 +56,11 @@ def log(msg):
 ATTN_SOURCES = ("api.cpp", "kernels.h", "kernels.hip")
 APPEND_SOURCES = ("api.cpp", "kernels.h", "append.hip")
 PREFILL_SOURCES = ("api.cpp", "kernels.h", "prefill.hip")
-MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
+STEP_SOURCES = ("api.cpp", "kernels.h", "kernels.hip", "append.hip")
+SOURCES_OF_OP = {"attn": ATTN_SOURCES, "append": APPEND_SOURCES, "prefill": PREFILL_SOURCES,
+                 "step": STEP_SOURCES}
+PREFIX_OF_OP = {"attn": "decode_attn", "append": "decode_attn_append",
+                "prefill": "decode_attn_prefill", "step": "decode_attn_step"}
 
 
 def kernel_source_hash(sources=ATTN_SOURCES) -> str:
@@ -55,11 +74,10 @@ def kernel_source_hash(sources=ATTN_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str, prefix: str = "decode_attn", sources=ATTN_SOURCES):
-    """HBM bytes per launch of the dominant kernel, from the committed rocprofv3 summary
-    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter reads for a
-    plain copy of known size), or None when there is none or the kernels changed since."""
-    path = os.path.join(PROFILES, f"{prefix}_{workload_name}.txt")
+def read_profile(workload_name: str, op: str = "attn"):
+    """The committed rocprofv3 summary of a workload as a dict of its top-level fields, or
+    (None, reason) when there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"{PREFIX_OF_OP[op]}_{workload_name}.txt")
     if not os.path.exists(path):
         return None, "no counter summary"
     fields = {}
@@ -68,48 +86,91 @@ def read_traffic(workload_name: str, prefix: str = "decode_attn", sources=ATTN_S
             if ":" in line and not line.startswith((" ", "#")):
                 k, v = line.split(":", 1)
                 fields.setdefault(k.strip(), v.strip())
-    if fields.get("kernel_source_sha256") != kernel_source_hash(sources):
+    if fields.get("kernel_source_sha256") != kernel_source_hash(SOURCES_OF_OP[op]):
         return None, "kernel changed since the counters were taken"
+    fields["_path"] = os.path.relpath(path, ROOT)
+    return fields, path
+
+
+def profile_traffic(fields):
     try:
-        return float(fields["traffic_bytes_per_launch"]), path
-    except (KeyError, ValueError):
-        return None, "summary lacks traffic_bytes_per_launch"
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, TypeError, ValueError):
+        return None
+
+
+def host_info():
+    """Cores this process may run on and the host CPU model."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return cores, model
+
+
+class _ThreadLimit:
+    """BLAS/OpenMP threads of the oracle's NumPy set to `n` (when threadpoolctl exists)."""
+
+    def __init__(self, n):
+        self.n, self.ctx = n, None
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self.ctx = threadpool_limits(limits=self.n)
+            self.ctx.__enter__()
+        except Exception:  # pragma: no cover
+            self.ctx = None
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
 
 
 def cpu_baseline(w, budget_s: float = 10.0):
-    """The fp64 oracle as it stands, timed on the host over a bounded sample."""
+    """The fp64 oracle as it stands, timed on the host over a bounded sample: a prefix of
+    the batch sized to about `budget_s` seconds, repeated while the budget lasts."""
     import numpy as np
     import oracle
     from decode_phase_attention_paged_amd.workload import ELEM_BYTES, SCALE_BYTES, kv_read_bytes
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    cores, model = host_info()
     c = w.config
-    # Sample: a prefix of the batch sized to fit the budget (at least one sequence).
-    t0 = time.perf_counter()
-    oracle.decode_attention(w.q[:1], w.k_pages, w.v_pages, w.block_table[:1], w.seq_lens[:1],
-                            w.scale, w.k_scale, w.v_scale)
-    per_token = max((time.perf_counter() - t0) / max(int(w.seq_lens[0]), 1), 1e-9)
-    total_tokens = int(w.seq_lens.sum())
-    n = c.batch
-    if per_token * total_tokens > budget_s:
-        cum = np.cumsum(w.seq_lens.astype(np.int64))
-        n = max(1, int(np.searchsorted(cum, budget_s / per_token)))
-    sample_bytes = kv_read_bytes(w.seq_lens[:n], c.n_kv_heads, c.head_dim,
-                                 ELEM_BYTES[c.kv_dtype], SCALE_BYTES[c.kv_dtype])
-    reps, spent = 0, 0.0
-    while reps < 1 or (spent < budget_s and reps < 50):
+    with _ThreadLimit(cores):
         t0 = time.perf_counter()
-        oracle.decode_attention(w.q[:n], w.k_pages, w.v_pages, w.block_table[:n], w.seq_lens[:n],
+        oracle.decode_attention(w.q[:1], w.k_pages, w.v_pages, w.block_table[:1], w.seq_lens[:1],
                                 w.scale, w.k_scale, w.v_scale)
-        spent += time.perf_counter() - t0
-        reps += 1
+        per_token = max((time.perf_counter() - t0) / max(int(w.seq_lens[0]), 1), 1e-9)
+        total_tokens = int(w.seq_lens.sum())
+        n = c.batch
+        if per_token * total_tokens > budget_s:
+            cum = np.cumsum(w.seq_lens.astype(np.int64))
+            n = max(1, int(np.searchsorted(cum, budget_s / per_token)))
+        sample_bytes = kv_read_bytes(w.seq_lens[:n], c.n_kv_heads, c.head_dim,
+                                     ELEM_BYTES[c.kv_dtype], SCALE_BYTES[c.kv_dtype])
+        reps, spent = 0, 0.0
+        while reps < 1 or (spent < budget_s and reps < 50):
+            t0 = time.perf_counter()
+            oracle.decode_attention(w.q[:n], w.k_pages, w.v_pages, w.block_table[:n],
+                                    w.seq_lens[:n], w.scale, w.k_scale, w.v_scale)
+            spent += time.perf_counter() - t0
+            reps += 1
     gbs = sample_bytes * reps / spent / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n} of {c.batch} sequences x {reps} repetitions "
-                      f"({sample_bytes * reps / 1e9:.3f} GB of KV in {spent:.1f} s)",
+                      f"({sample_bytes * reps / 1e9:.3f} GB of KV in {spent:.1f} s); NumPy "
+                      f"float64, BLAS threads limited to the {cores} cores of this "
+                      f"process's affinity mask",
+            "cpu_model": model,
             "seconds_per_full_step": round(spent / reps * total_tokens /
                                            max(int(w.seq_lens[:n].sum()), 1), 4)}
 
@@ -142,9 +203,51 @@ def device_tensor(torch, np, a, dev):
     return t.view(torch.float8_e4m3fn) if a.dtype == np.uint8 else t
 
 
+def replicas_for(args, pool_bytes: int) -> int:
+    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+    return min(reps, max(1, (48 << 30) // pool_bytes))
+
+
+def timed_windows(torch, stream, step, steps: int, windows: int, first: int):
+    """`windows` timed windows of exactly `steps` back-to-back calls of step(i), each
+    between one pair of HIP events recorded on `stream` (the stream the library launches
+    on), with a device synchronisation before and after. No event sits between steps: an
+    event record between two launches delays the second one by several microseconds on
+    this GPU. Returns (ms per window, host wall seconds per window)."""
+    total_ms, walls = [], []
+    i = first
+    for _ in range(windows):
+        start_ev = torch.cuda.Event(enable_timing=True)
+        stop_ev = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start_ev.record(stream)
+        for _ in range(steps):
+            step(i)
+            i += 1
+        stop_ev.record(stream)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - wall0)
+        total_ms.append(start_ev.elapsed_time(stop_ev))
+    return total_ms, walls
+
+
+def window_stats(total_ms, steps):
+    per = sorted(t / steps for t in total_ms)
+    return {"median_ms": statistics.median(per), "min_ms": per[0], "max_ms": per[-1]}
+
+
+def default_windows(steps: int) -> int:
+    """At least five windows and at least 100 timed steps in all."""
+    return max(5, math.ceil(100 / max(steps, 1)))
+
+
 # Kernels one step launches, by plan mode (stream, split, segment).
-KERNELS = {0: "stream_kernel + piece_merge_kernel", 1: "split_kernel + split_merge_kernel",
-           2: "seg_kernel"}
+def kernel_names(mode: int, kv: str, group: int):
+    t = f"<{kv},G={group}>"
+    return {0: [f"stream_kernel{t}", "piece_merge_kernel"],
+            1: [f"split_kernel{t}", "split_merge_kernel"],
+            2: [f"seg_kernel{t}"]}[mode]
 
 
 def main():
@@ -152,9 +255,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8],
-                    help="workload preset (0 = the op's default: 2 for attn and append, "
-                         "8 for prefill)")
+    ap.add_argument("--repeats", type=int, default=0,
+                    help="timed windows of --steps steps each (0 = max(5, ceil(100/steps)))")
+    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8, 9],
+                    help="workload preset (0 = the op's default: 3 for attn, 2 for append "
+                         "and step, 8 for prefill)")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="stream mode on this many workgroups, or the grid of segment mode "
                          "with --splits 1 (0 = the library's plan)")
@@ -162,6 +267,8 @@ def main():
                     help="1 = segment mode, >1 = split mode with this many partitions "
                          "(0 = the library's plan)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
+    ap.add_argument("--no-hot", action="store_true",
+                    help="skip the labelled one-replica (hot pool) figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--graph", type=int, default=0,
@@ -171,10 +278,18 @@ def main():
                     help="prefill only: run the preset's shapes over another storage format")
     ap.add_argument("--op", choices=["attn", "append", "prefill", "step"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
-                         "that precedes it in a decode step, on the same workload; prefill: "
-                         "chunked-prefill attention (default workload: the prefill preset)")
+                         "that precedes it in a decode step, on the same workload; step: "
+                         "append then attention; prefill: chunked-prefill attention")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write profiles/<op>_<workload>.txt from the rocprofv3 CSVs in DIR")
+    ap.add_argument("--tag", default=None, help="with --summarize-profile: the run's tag")
     args = ap.parse_args()
 
+    if args.summarize_profile:
+        if not args.tag:
+            ap.error("--summarize-profile needs --tag")
+        summarize_profile(args.summarize_profile, args.tag)
+        return
     if args.kv is not None and args.op != "prefill":
         ap.error("--kv applies to --op prefill only; the decode presets fix their formats")
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -183,6 +298,8 @@ def main():
               "MI355X, and multi-GPU sharding is a design note only; run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.repeats <= 0:
+        args.repeats = default_windows(args.steps)
 
     import numpy as np
     import torch
@@ -195,7 +312,7 @@ def main():
 
     lib = binding.load_library()
     if args.config == 0:
-        args.config = 8 if args.op == "prefill" else 2
+        args.config = DEFAULT_CONFIG[args.op]
     cfg = CONFIGS[args.config]
     if args.op == "append":
         return bench_append(args, cfg, lib, torch, np, binding, generate)
@@ -210,8 +327,7 @@ def main():
     t = lambda a: device_tensor(torch, np, a, dev)
     q, bt, sl = t(w.q), t(w.block_table), t(w.seq_lens)
     pool_bytes = 2 * w.k_pages.nbytes + (2 * w.k_scale.nbytes if w.k_scale is not None else 0)
-    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
-    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    reps = replicas_for(args, pool_bytes)
     pools = []
     for _ in range(reps):
         pools.append((t(w.k_pages), t(w.v_pages), t(w.k_scale), t(w.v_scale)))
@@ -222,6 +338,8 @@ def main():
     plan = binding.plan(cfg.batch, cfg.max_blocks_per_seq, cfg.n_q_heads, cfg.n_kv_heads,
                         cfg.block_size, cfg.kv_dtype, args.workgroups, args.splits, num_cus)
     explicit = bool(args.workgroups or args.splits)
+    group = cfg.n_q_heads // cfg.n_kv_heads
+    kernels = kernel_names(plan.mode, cfg.kv_dtype, group)
 
     # Marshal the arguments once; the timed loop calls the C ABI directly.
     p = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
@@ -241,22 +359,24 @@ def main():
         else:
             call_args.append(("auto", common + (s_handle,)))
 
-    def step(i):
-        kind, a = call_args[i % reps]
+    def call(kind, a):
         st = lib.decode_attn(*a) if kind == "auto" else lib.decode_attn_ex(*a)
         if st != 0:
             raise RuntimeError(f"decode_attn failed: {binding.STATUS.get(st, st)}")
 
+    rotate = lambda i: call(*call_args[i % reps])
+    hot = lambda i: call(*call_args[0])
+
     log(f"plan: {plan} replicas={reps} "
         f"pool={pool_bytes / 1e6:.1f} MB kv_bytes/step={w.kv_bytes / 1e6:.1f} MB")
     for i in range(args.warmup):
-        step(i)
+        rotate(i)
     torch.cuda.synchronize()
 
-    graph = None
+    step = rotate
     if args.graph > 0:
         # The same calls, recorded on a capture stream, args.graph steps per graph; replays
-        # run on torch's current stream, where the events below are recorded.
+        # run on torch's current stream, where the events are recorded.
         cap = torch.cuda.Stream()
         handle = ctypes.c_void_p(cap.cuda_stream)
         captured = [(kind, a[:-1] + (handle,)) for kind, a in call_args]
@@ -264,54 +384,56 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=cap):
             for i in range(args.graph):
-                kind, a = captured[i % reps]
-                st = lib.decode_attn(*a) if kind == "auto" else lib.decode_attn_ex(*a)
-                if st != 0:
-                    raise RuntimeError(f"decode_attn failed in capture: {binding.STATUS.get(st, st)}")
+                call(*captured[i % reps])
         torch.cuda.synchronize()
         args.steps = -(-args.steps // args.graph) * args.graph
         graph.replay()
         torch.cuda.synchronize()
-        log(f"graph: {args.graph} steps per replay, {args.steps // args.graph} replays timed")
-
-    # Timed region: exactly K back-to-back steps between one pair of HIP events recorded
-    # on the launch stream. No event sits between steps: an event record between two
-    # launches delays the second one by several microseconds on this GPU.
-    start_ev = torch.cuda.Event(enable_timing=True)
-    stop_ev = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start_ev.record(stream)
-    if graph is not None:
-        for _ in range(args.steps // args.graph):
-            graph.replay()
+        log(f"graph: {args.graph} steps per replay")
+        replays = args.steps // args.graph
+        step = lambda i: graph.replay()
+        steps_per_window, scale_steps = replays, args.graph
     else:
-        for i in range(args.steps):
-            step(args.warmup + i)
-    stop_ev.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start_ev.elapsed_time(stop_ev)
-    ms_per_step = total_ms / args.steps
-    # A step is the main kernel and the merge launched right behind it; back-to-back
-    # launches leave no gap, so the step time is the kernels' summed duration and is taken,
-    # conservatively, as the duration of the dominant (main) launch.
-    avg_launch_s = ms_per_step / 1e3
-    gbs = w.kv_bytes * args.steps / (total_ms / 1e3) / 1e9
-    achieved = w.kv_bytes / avg_launch_s / 1e9
-    log(f"steps={args.steps} total={total_ms:.3f} ms (wall {wall * 1e3:.1f} ms) "
-        f"us/step={ms_per_step * 1e3:.2f} GB/s={gbs:.1f} ({gbs / HBM_PEAK_GBS:.3f} of peak)")
-    if wall * 1e3 > 1.5 * total_ms:
+        steps_per_window, scale_steps = args.steps, 1
+
+    total_ms, walls = timed_windows(torch, stream, step, steps_per_window, args.repeats,
+                                    args.warmup)
+    st = window_stats(total_ms, steps_per_window * scale_steps)
+    ms_per_step = st["median_ms"]
+    gbs = w.kv_bytes / (ms_per_step / 1e3) / 1e9
+    log(f"{args.repeats} windows x {args.steps} steps: us/step median {ms_per_step * 1e3:.2f} "
+        f"[{st['min_ms'] * 1e3:.2f}, {st['max_ms'] * 1e3:.2f}]  GB/s={gbs:.1f} "
+        f"({gbs / HBM_PEAK_GBS:.4f} of peak)")
+    if max(walls) * 1e3 > 1.5 * max(total_ms):
         log("warning: host launch rate may be limiting the step rate")
 
-    traffic, traffic_src = read_traffic(cfg.name)
-    log(f"traffic: {traffic} ({traffic_src})")
+    hot_rec = None
+    if not args.no_hot and args.graph == 0:
+        for i in range(args.warmup):
+            hot(i)
+        hot_ms, _ = timed_windows(torch, stream, hot, args.steps, args.repeats, 0)
+        hs = window_stats(hot_ms, args.steps)
+        hot_rec = {"us_per_step": round(hs["median_ms"] * 1e3, 3),
+                   "gbs": round(w.kv_bytes / (hs["median_ms"] / 1e3) / 1e9, 2),
+                   "replicas": 1,
+                   "note": "hot: every step reads the same pool replica, so up to 256 MB of it "
+                           "may be served by the Infinity Cache; not the headline"}
+        log(f"hot (one replica): us/step {hot_rec['us_per_step']} GB/s {hot_rec['gbs']}")
+
+    prof, prof_src = read_profile(cfg.name, "attn")
+    traffic = profile_traffic(prof) if prof else None
+    log(f"profile: {prof_src}")
     baseline = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         baseline = cpu_baseline(w)
         log(f"cpu baseline: {baseline}")
 
+    launches = len(kernels)
+    # One launch per step: the step time is that kernel's average launch duration
+    # (back-to-back launches leave no gap). Two launches: the step time is the sum of both,
+    # a conservative stand-in for the main kernel's duration, which the profile splits out.
+    achieved = w.kv_bytes / (ms_per_step / 1e3) / 1e9
     record = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -319,14 +441,17 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_min_max": [round(st["min_ms"] * 1e3, 3), round(st["max_ms"] * 1e3, 3)],
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
+        "argv": sys.argv[1:],
         "config": {
             "workload": cfg.name,
             "batch": cfg.batch, "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
@@ -346,9 +471,19 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": KERNELS[plan.mode] + " (one step)",
-            "avg_launch_us": round(avg_launch_s * 1e6, 3),
+            "kernel": kernels[0],
+            "launches_per_step": launches,
+            "avg_launch_us": round(ms_per_step * 1e3, 3) if launches == 1 else None,
+            "step_us": round(ms_per_step * 1e3, 3),
+            "achieved_from": "median step time (= the kernel's launch duration)" if launches == 1
+                             else "median step time of both launches (conservative)",
+            "profile": None if not prof else {
+                "file": prof["_path"],
+                "dominant_kernel_avg_us": round(float(prof["dominant_kernel_timed_avg_ns"]) / 1e3, 3),
+                "traffic_over_algorithmic": float(prof["traffic_over_algorithmic"]),
+            },
         },
+        "hot": hot_rec,
         "cpu_baseline": baseline,
     }
     print(json.dumps(record), flush=True)
@@ -367,26 +502,25 @@ def append_cpu_baseline(w, table, positions, new, budget_s: float = 10.0):
     """oracle.append_kv as it stands, timed on the host over whole launches."""
     import oracle
     c = w.config
+    cores, model = host_info()
     reps, spent = 0, 0.0
-    while reps < 1 or (spent < budget_s and reps < 200):
-        t0 = time.perf_counter()
-        oracle.append_kv(w.k_pages, w.v_pages, table, positions, new[0], new[1], c.block_size,
-                         w.k_scale, w.v_scale)
-        spent += time.perf_counter() - t0
-        reps += 1
+    with _ThreadLimit(cores):
+        while reps < 1 or (spent < budget_s and reps < 200):
+            t0 = time.perf_counter()
+            oracle.append_kv(w.k_pages, w.v_pages, table, positions, new[0], new[1],
+                             c.block_size, w.k_scale, w.v_scale)
+            spent += time.perf_counter() - t0
+            reps += 1
     nbytes = append_bytes(c.batch, c.n_kv_heads, c.head_dim, c.kv_dtype)
-    return {"value": round(nbytes * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+    return {"value": round(nbytes * reps / spent / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{reps} whole launches ({c.batch * c.n_kv_heads} rows each) in "
                       f"{spent:.1f} s, pool copies included"}
 
 
-def bench_append(args, cfg, lib, torch, np, binding, generate):
-    """Time decode_attn_append: every sequence of the workload writes its next token
-    (position L_b) into its page slot; sequences whose next token starts a new page get a
-    fresh page. The new rows are fp16 ~ N(0, 1) scaled per row by U(0.1, 10)."""
-    log(f"generating {cfg.name} for the append ...")
-    w = generate(cfg)
+def grow_for_append(w, np, cfg):
+    """Positions L_b for every sequence's next token, with a fresh page (numbered past the
+    pool) where that token starts one. Returns (table, positions, fresh)."""
     table = w.block_table.copy()
     positions = w.seq_lens.astype(np.int32).copy()
     fresh = 0
@@ -397,6 +531,26 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
         elif table[b, j] < 0:
             table[b, j] = w.num_pages + fresh
             fresh += 1
+    return table, positions, fresh
+
+
+def timed_record(args, torch, stream, step, nbytes):
+    """Warm-up, then the timed windows; returns (median ms/step, stats)."""
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    total_ms, _ = timed_windows(torch, stream, step, args.steps, args.repeats, args.warmup)
+    st = window_stats(total_ms, args.steps)
+    return st["median_ms"], st
+
+
+def bench_append(args, cfg, lib, torch, np, binding, generate):
+    """Time decode_attn_append: every sequence of the workload writes its next token
+    (position L_b) into its page slot; sequences whose next token starts a new page get a
+    fresh page. The new rows are fp16 ~ N(0, 1) scaled per row by U(0.1, 10)."""
+    log(f"generating {cfg.name} for the append ...")
+    w = generate(cfg)
+    table, positions, fresh = grow_for_append(w, np, cfg)
     n_pages = w.num_pages + fresh
     rng = np.random.default_rng(w.seed + 1)
     shape = (cfg.batch, cfg.n_kv_heads, cfg.head_dim)
@@ -412,8 +566,7 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
             "fp8": torch.float8_e4m3fn}[cfg.kv_dtype]
     pool_bytes = 2 * n_pages * cfg.n_kv_heads * cfg.block_size * (
         cfg.head_dim * (1 if scaled else 2) + (4 if scaled else 0))
-    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
-    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    reps = replicas_for(args, pool_bytes)
     t = lambda a: device_tensor(torch, np, a, dev)
     bt, pos = t(table), t(positions)
     sets = []
@@ -440,24 +593,12 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
     nbytes = append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.kv_dtype)
     log(f"append: rows={cfg.batch * cfg.n_kv_heads} fresh_pages={fresh} replicas={reps} "
         f"bytes/launch={nbytes}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    stop_ev = torch.cuda.Event(enable_timing=True)
-    start_ev.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    stop_ev.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start_ev.elapsed_time(stop_ev)
-    ms_per_step = total_ms / args.steps
-    gbs = nbytes * args.steps / (total_ms / 1e3) / 1e9
-    log(f"steps={args.steps} total={total_ms:.3f} ms us/step={ms_per_step * 1e3:.2f} "
-        f"GB/s={gbs:.1f}")
-    traffic, traffic_src = read_traffic(cfg.name, prefix="decode_attn_append",
-                                       sources=APPEND_SOURCES)
-    log(f"traffic: {traffic} ({traffic_src})")
+    ms_per_step, st = timed_record(args, torch, stream, step, nbytes)
+    gbs = nbytes / (ms_per_step / 1e3) / 1e9
+    log(f"us/launch median {ms_per_step * 1e3:.2f} GB/s={gbs:.1f}")
+    prof, prof_src = read_profile(cfg.name, "append")
+    traffic = profile_traffic(prof) if prof else None
+    log(f"profile: {prof_src}")
     baseline = None
     if not args.no_cpu_baseline:
         w_host = w
@@ -476,14 +617,17 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_min_max": [round(st["min_ms"] * 1e3, 3), round(st["max_ms"] * 1e3, 3)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"fp16": "f16", "bf16": "bf16", "int8": "f16->i8",
                   "fp8": "f16->fp8e4m3"}[cfg.kv_dtype],
         "data": "synthetic",
+        "argv": sys.argv[1:],
         "config": {"workload": cfg.name + "_append", "batch": cfg.batch,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
@@ -491,11 +635,11 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
                    "bytes_per_launch": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "append_kernel", "avg_launch_us": round(ms_per_step * 1e3, 3)},
+                     "kernel": "append_kernel", "launches_per_step": 1,
+                     "avg_launch_us": round(ms_per_step * 1e3, 3)},
         "cpu_baseline": baseline,
     }
     print(json.dumps(record), flush=True)
-
 
 
 def bench_step(args, cfg, lib, torch, np, binding, generate):
@@ -506,16 +650,7 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
     from decode_phase_attention_paged_amd.workload import ELEM_BYTES, SCALE_BYTES, kv_read_bytes
     log(f"generating {cfg.name} for a decode step ...")
     w = generate(cfg)
-    table = w.block_table.copy()
-    positions = w.seq_lens.astype(np.int32).copy()
-    fresh = 0
-    for b in range(cfg.batch):
-        j = int(positions[b]) // cfg.block_size
-        if j >= table.shape[1]:
-            positions[b] = int(positions[b]) - 1      # a full table: rewrite the last slot
-        elif table[b, j] < 0:
-            table[b, j] = w.num_pages + fresh
-            fresh += 1
+    table, positions, fresh = grow_for_append(w, np, cfg)
     lens = (positions + 1).astype(np.int32)
     n_pages = w.num_pages + fresh
     grow = lambda a: None if a is None else np.concatenate(
@@ -532,8 +667,7 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
     t = lambda a: device_tensor(torch, np, a, dev)
     q, bt, pos, sl, kn, vn = (t(a) for a in (w.q, table, positions, lens, new[0], new[1]))
     pool_bytes = 2 * k_host.nbytes + (2 * ks_host.nbytes if ks_host is not None else 0)
-    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
-    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    reps = replicas_for(args, pool_bytes)
     pools = [(t(k_host), t(v_host), t(ks_host), t(vs_host)) for _ in range(reps)]
     out = torch.empty(w.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -561,20 +695,9 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
                              SCALE_BYTES[cfg.kv_dtype])
     nbytes = kv_bytes + append_bytes(cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.kv_dtype)
     log(f"step: fresh_pages={fresh} replicas={reps} bytes/step={nbytes}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    stop_ev = torch.cuda.Event(enable_timing=True)
-    start_ev.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    stop_ev.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start_ev.elapsed_time(stop_ev)
-    ms_per_step = total_ms / args.steps
-    gbs = nbytes * args.steps / (total_ms / 1e3) / 1e9
-    log(f"steps={args.steps} us/step={ms_per_step * 1e3:.2f} GB/s={gbs:.1f}")
+    ms_per_step, st = timed_record(args, torch, stream, step, nbytes)
+    gbs = nbytes / (ms_per_step / 1e3) / 1e9
+    log(f"us/step median {ms_per_step * 1e3:.2f} GB/s={gbs:.1f}")
     record = {
         "metric": "decode step (K/V append + attention) GB/s (fraction of MI355X HBM peak) + µs/step",
         "value": round(gbs, 2),
@@ -582,13 +705,16 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_min_max": [round(st["min_ms"] * 1e3, 3), round(st["max_ms"] * 1e3, 3)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
+        "argv": sys.argv[1:],
         "config": {"workload": cfg.name + "_step", "batch": cfg.batch,
                    "n_q_heads": cfg.n_q_heads, "n_kv_heads": cfg.n_kv_heads,
                    "head_dim": cfg.head_dim, "block_size": cfg.block_size,
@@ -596,11 +722,12 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
                    "bytes_per_step": int(nbytes)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "append_kernel + attention (two launches)",
-                     "avg_launch_us": None},
+                     "kernel": "append_kernel + attention", "launches_per_step": None,
+                     "avg_launch_us": None, "step_us": round(ms_per_step * 1e3, 3)},
         "cpu_baseline": None,
     }
     print(json.dumps(record), flush=True)
+
 
 def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
     """oracle.prefill_attention as it stands, timed on the host over whole sequences."""
@@ -608,26 +735,23 @@ def prefill_cpu_baseline(w, q, q_start, budget_s: float = 10.0):
     import oracle
     from decode_phase_attention_paged_amd.workload import prefill_flops
     c = w.config
+    cores, model = host_info()
     done_flops, spent, seqs = 0, 0.0, 0
     order = np.argsort(w.seq_lens)
-    for b in order:
-        rows = slice(int(q_start[b]), int(q_start[b + 1]))
-        sub = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
-        t0 = time.perf_counter()
-        oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
-                                 w.seq_lens[b:b + 1], sub, w.scale, w.k_scale, w.v_scale)
-        spent += time.perf_counter() - t0
-        done_flops += prefill_flops(w.seq_lens[b:b + 1], sub, c.n_q_heads, c.head_dim)
-        seqs += 1
-        if spent >= budget_s:
-            break
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    return {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    with _ThreadLimit(cores):
+        for b in order:
+            rows = slice(int(q_start[b]), int(q_start[b + 1]))
+            sub = np.array([0, q_start[b + 1] - q_start[b]], dtype=np.int32)
+            t0 = time.perf_counter()
+            oracle.prefill_attention(q[rows], w.k_pages, w.v_pages, w.block_table[b:b + 1],
+                                     w.seq_lens[b:b + 1], sub, w.scale, w.k_scale, w.v_scale)
+            spent += time.perf_counter() - t0
+            done_flops += prefill_flops(w.seq_lens[b:b + 1], sub, c.n_q_heads, c.head_dim)
+            seqs += 1
+            if spent >= budget_s:
+                break
+    return {"value": round(done_flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "cpu_model": model,
             "sample": f"{seqs} of {c.batch} sequences, shortest first ({spent:.1f} s)"}
 
 
@@ -649,8 +773,7 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
     t = lambda a: device_tensor(torch, np, a, dev)
     q, qs, bt, sl = t(q_host), t(qs_host), t(w.block_table), t(w.seq_lens)
     pool_bytes = 2 * w.k_pages.nbytes
-    reps = args.replicas or max(2, math.ceil((1 << 30) / pool_bytes))
-    reps = min(reps, max(1, (48 << 30) // pool_bytes))
+    reps = replicas_for(args, pool_bytes)
     pools = [(t(w.k_pages), t(w.v_pages)) for _ in range(reps)]
     ks, vs = t(w.k_scale), t(w.v_scale)
     out = torch.empty(q_host.shape, dtype=torch.float32, device=dev)
@@ -672,24 +795,13 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
             raise RuntimeError(f"decode_attn_prefill failed: {binding.STATUS.get(st, st)}")
 
     log(f"prefill: rows={total} chunk={cfg.chunk} replicas={reps} flops/step={flops / 1e9:.1f} G")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    stop_ev = torch.cuda.Event(enable_timing=True)
-    start_ev.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    stop_ev.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start_ev.elapsed_time(stop_ev)
-    ms_per_step = total_ms / args.steps
+    ms_per_step, st = timed_record(args, torch, stream, step, flops)
     tflops = flops / (ms_per_step / 1e3) / 1e12
-    log(f"steps={args.steps} total={total_ms:.3f} ms us/step={ms_per_step * 1e3:.2f} "
-        f"TFLOP/s={tflops:.1f} ({tflops / MFMA_F16_PEAK_TFLOPS:.3f} of peak)")
-    traffic, traffic_src = read_traffic(cfg.name, prefix="decode_attn_prefill",
-                                        sources=PREFILL_SOURCES)
-    log(f"traffic: {traffic} ({traffic_src})")
+    log(f"us/launch median {ms_per_step * 1e3:.2f} TFLOP/s={tflops:.1f} "
+        f"({tflops / MFMA_F16_PEAK_TFLOPS:.3f} of peak)")
+    prof, prof_src = read_profile(cfg.name, "prefill")
+    traffic = profile_traffic(prof) if prof else None
+    log(f"profile: {prof_src}")
     baseline = None
     if not args.no_cpu_baseline:
         baseline = prefill_cpu_baseline(w, q_host, qs_host)
@@ -701,13 +813,16 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_min_max": [round(st["min_ms"] * 1e3, 3), round(st["max_ms"] * 1e3, 3)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": DTYPE_NAMES[cfg.kv_dtype],
         "data": "synthetic",
+        "argv": sys.argv[1:],
         "config": {"workload": cfg.name, "batch": cfg.batch, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype, "chunk": cfg.chunk,
@@ -718,10 +833,232 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "prefill_kernel", "avg_launch_us": round(ms_per_step * 1e3, 3)},
+                     "kernel": "prefill_kernel", "launches_per_step": 1,
+                     "avg_launch_us": round(ms_per_step * 1e3, 3)},
         "cpu_baseline": baseline,
     }
     print(json.dumps(record), flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# Profile summaries. Layout of DIR for one workload tagged TAG (each a rocprofv3 output
+# directory written with `-d DIR/<name> -o run --output-format csv`, next to the bench.py
+# JSON line the profiled run printed, DIR/<name>.json):
+#   trace_TAG               --kernel-trace --stats
+#   pmc_FETCH_SIZE_TAG      --pmc FETCH_SIZE
+#   pmc_WRITE_SIZE_TAG      --pmc WRITE_SIZE
+#   pmc_FETCH_SIZE_copy, pmc_WRITE_SIZE_copy   the same counters over bench.py --copy-calibration
+#   pmc_<P>_TAG             optional further counter passes (any name P), e.g. the SQ and
+#                           TCC/TCP sets below
+COUNTER_PASSES = {
+    "sq_a": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY",
+             "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU",
+             "GRBM_GUI_ACTIVE"],
+    "sq_b": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_SMEM",
+             "SQ_ACTIVE_INST_VMEM", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VMEM",
+             "GRBM_GUI_ACTIVE"],
+    "mem": ["TCC_HIT_sum", "TCC_MISS_sum", "TCP_UTCL1_TRANSLATION_MISS_sum",
+            "TCP_UTCL1_TRANSLATION_HIT_sum", "TCP_TCC_READ_REQ_sum"],
+}
+
+
+def _csv_rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _last_json(path):
+    with open(path) as f:
+        lines = [ln for ln in f.read().strip().splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1])
+
+
+def _pmc(dirpath):
+    """{kernel: {counter: [value per dispatch]}} of one --pmc output directory."""
+    by = {}
+    for r in _csv_rows(os.path.join(dirpath, "run_counter_collection.csv")):
+        by.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    return by
+
+
+def _mean(v):
+    return sum(v) / len(v) if v else 0.0
+
+
+def summarize_profile(d: str, tag: str):
+    d = os.path.abspath(d)
+    trace_dir = os.path.join(d, f"trace_{tag}")
+    rec = _last_json(os.path.join(d, f"trace_{tag}.json"))
+    argv = [a for a in rec.get("argv", []) if a]
+    op = "attn"
+    if "--op" in argv:
+        op = argv[argv.index("--op") + 1]
+    elif "prefill" in rec["metric"]:
+        op = "prefill"
+    elif "append" in rec["metric"]:
+        op = "append" if rec["metric"].startswith("decode K/V append") else "step"
+    workload = rec["config"]["workload"]
+    for suffix in ("_append", "_step"):
+        if op != "attn" and workload.endswith(suffix):
+            workload = workload[: -len(suffix)]
+    prefix = PREFIX_OF_OP[op]
+    timed = rec["steps"] * rec.get("repeats", 1)
+
+    rows = _csv_rows(os.path.join(trace_dir, "run_kernel_trace.csv"))
+    by, res = {}, {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if name.startswith("__amd") or "elementwise" in name or "Memcpy" in name:
+            continue
+        by.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        res[name] = (r.get("VGPR_Count"), r.get("Accum_VGPR_Count"), r.get("SGPR_Count"),
+                     r.get("LDS_Block_Size"), r.get("Scratch_Size"), r.get("Grid_Size_X"),
+                     r.get("Workgroup_Size_X"))
+    passes = {}
+    for name in sorted(os.listdir(d)):
+        full = os.path.join(d, name)
+        if name.startswith("pmc_") and name.endswith("_" + tag) and os.path.isdir(full):
+            passes[name[4:-len(tag) - 1]] = _pmc(full)
+
+    def counters_of(kernel):
+        merged = {}
+        for pname, pk in passes.items():
+            for cname, vals in pk.get(kernel, {}).items():
+                merged.setdefault(cname, vals)
+        return merged
+
+    cf, cw = _pmc(os.path.join(d, "pmc_FETCH_SIZE_copy")), _pmc(os.path.join(d, "pmc_WRITE_SIZE_copy"))
+    fmax = max(max(v.get("FETCH_SIZE", [0.0])) for v in cf.values())
+    wmax = max(max(v.get("WRITE_SIZE", [0.0])) for v in cw.values())
+    fetch_scale = (1 << 30) / 1024 / fmax
+    write_scale = (1 << 30) / 1024 / wmax
+
+    base_cmd = "python3 $REPO/bench.py " + " ".join(
+        a for a in argv)
+    out = [f"# rocprofv3 summary: {prefix}, workload {workload}",
+           f"# {json.dumps(rec['config'])}",
+           "# $REPO is the repository root; each command runs from /tmp with TMPDIR=/tmp.",
+           f"# summarised by: python3 $REPO/bench.py --summarize-profile $REPO/gpurun_out/prof --tag {tag}",
+           f"command_trace: rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof/trace_{tag} -o run -- {base_cmd}"]
+    for pname, pk in passes.items():
+        names = sorted({c for k in pk.values() for c in k})
+        pj = os.path.join(d, f"pmc_{pname}_{tag}.json")
+        pargv = " ".join(_last_json(pj).get("argv", [])) if os.path.exists(pj) else " ".join(argv)
+        out.append(f"command_pmc_{pname}: rocprofv3 --pmc {' '.join(names)} --output-format csv "
+                   f"-d $REPO/gpurun_out/prof/pmc_{pname}_{tag} -o run -- python3 $REPO/bench.py {pargv}")
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        out.append(f"command_copy_{c.split('_')[0].lower()}: rocprofv3 --pmc {c} --output-format csv "
+                   f"-d $REPO/gpurun_out/prof/pmc_{c}_copy -o run -- python3 $REPO/bench.py --copy-calibration")
+    out.append(f"kernel_source_sha256: {kernel_source_hash(SOURCES_OF_OP[op])}")
+    out.append("")
+    out.append(f"## kernel trace (per launch; \"timed\" = the last {timed} launches of each kernel, "
+               f"the ones bench.py times)")
+    dom, dom_total, stats = None, -1, {}
+    for k, v in by.items():
+        tv = v[-timed:]
+        avg, tavg = _mean(v), _mean(tv)
+        ctr = counters_of(k)
+        stats[k] = (avg, tavg, ctr)
+        vg, ag, sg, lds, scr, grid, wg = res[k]
+        out.append(f"kernel: {k}")
+        out.append(f"  calls {len(v)}  avg_ns {avg:.1f}  timed_avg_ns {tavg:.1f}  min_ns {min(v)}  "
+                   f"max_ns {max(v)}  median_ns {statistics.median(v):.0f}")
+        out.append(f"  resources: vgpr {vg} agpr {ag} sgpr {sg} lds_bytes {lds} scratch_bytes {scr} "
+                   f"grid_threads {grid} workgroup {wg}")
+        for cname in sorted(ctr):
+            out.append(f"  {cname}_per_dispatch {_mean(ctr[cname]):.2f}")
+        if sum(v) > dom_total:
+            dom, dom_total = k, sum(v)
+    out.append("")
+    out.append("## copy calibration (torch copy of 1 GiB: reads 1 GiB, writes 1 GiB)")
+    out.append(f"copy_fetch_kib_per_dispatch: {fmax:.2f}")
+    out.append(f"copy_write_kib_per_dispatch: {wmax:.2f}")
+    out.append(f"fetch_scale: {fetch_scale:.4f}")
+    out.append(f"write_scale: {write_scale:.4f}")
+    out.append("")
+    avg, tavg, ctr = stats[dom]
+    fa, wa = _mean(ctr.get("FETCH_SIZE", [])), _mean(ctr.get("WRITE_SIZE", []))
+    traffic = (fa * fetch_scale + wa * write_scale) * 1024
+    cfg = rec["config"]
+    out.append("## figures used by bench.py (dominant kernel)")
+    out.append(f"dominant_kernel: {dom}")
+    out.append(f"dominant_kernel_avg_ns: {avg:.1f}")
+    out.append(f"dominant_kernel_timed_avg_ns: {tavg:.1f}")
+    out.append(f"bench_us_per_step_in_this_run: {rec['us_per_step']}")
+    if op == "prefill":
+        kv = cfg["kv_bytes_per_step"]
+        qo = cfg["rows"] * cfg["n_q_heads"] * cfg["head_dim"] * (2 + 4)   # q 16-bit, out fp32
+        alg = kv + qo
+        out.append(f"algorithmic_flops_per_launch: {cfg['flops_per_step']}")
+        out.append(f"algorithmic_bytes_per_launch: {alg}  (K/V {kv} + q 16-bit and out fp32 {qo})")
+        out.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+        out.append(f"traffic_over_algorithmic: {traffic / alg:.4f}")
+        out.append(f"achieved_tflops_at_trace_timed_avg: {cfg['flops_per_step'] / tavg / 1e3:.1f}")
+    else:
+        alg = cfg.get("kv_bytes_per_step", cfg.get("bytes_per_launch"))
+        out.append(f"algorithmic_bytes_per_launch: {alg}")
+        out.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+        out.append(f"traffic_over_algorithmic: {traffic / alg:.4f}")
+        out.append(f"achieved_gbs_at_trace_timed_avg: {alg / tavg:.1f}")
+        out.append(f"frac_of_hbm_peak_at_trace_timed_avg: {alg / tavg / HBM_PEAK_GBS:.4f}")
+    derived = derived_counters(ctr, tavg)
+    if derived:
+        out.append("")
+        out.append("## derived from the counter passes (dominant kernel, per dispatch)")
+        for k, v in derived:
+            out.append(f"{k}: {v}")
+    path = os.path.join(PROFILES, f"{prefix}_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}: {dom[:70]} timed avg {tavg / 1e3:.2f} us, "
+          f"traffic/alg {traffic / alg:.4f}")
+
+
+# MI355X: 256 compute units of 4 SIMDs in 8 XCDs; SQ cycle counters count quad-cycles.
+N_CU, N_SIMD, N_XCD, CLOCK_GHZ = 256, 1024, 8, 2.4
+
+
+def derived_counters(ctr, kernel_ns):
+    """Readable figures from the raw counters of one kernel, where they were collected.
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's busy cycles are a eighth of it;
+    SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_* count quad-cycles summed over all waves."""
+    m = {k: _mean(v) for k, v in ctr.items()}
+    out = []
+    gui = m.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cycles = gui / N_XCD
+        out.append(("gpu_busy_cycles", f"{cycles:.0f}  ({cycles / kernel_ns:.2f} per ns of the "
+                                       f"traced kernel time)"))
+        if "SQ_WAVE_CYCLES" in m:
+            out.append(("mean_resident_waves_per_cu",
+                        f"{4 * m['SQ_WAVE_CYCLES'] / (cycles * N_CU):.2f}"))
+        if "SQ_ACTIVE_INST_VALU" in m:
+            out.append(("valu_busy_fraction_per_simd",
+                        f"{4 * m['SQ_ACTIVE_INST_VALU'] / (cycles * N_SIMD):.3f}"))
+        if "SQ_ACTIVE_INST_VMEM" in m:
+            out.append(("vmem_issue_fraction_per_simd",
+                        f"{4 * m['SQ_ACTIVE_INST_VMEM'] / (cycles * N_SIMD):.3f}"))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out.append(("mfma_busy_fraction_per_simd",
+                        f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * N_SIMD):.3f}"))
+    if m.get("SQ_WAVE_CYCLES"):
+        for k in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY"):
+            if k in m:
+                out.append((k.lower() + "_over_wave_cycles", f"{m[k] / m['SQ_WAVE_CYCLES']:.3f}"))
+    if m.get("SQ_WAVES"):
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_SALU", "SQ_INSTS_SMEM",
+                  "SQ_INSTS_LDS", "SQ_INSTS_MFMA"):
+            if k in m:
+                out.append((k.lower() + "_per_wave", f"{m[k] / m['SQ_WAVES']:.1f}"))
+    if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and m["TCC_HIT_sum"] + m["TCC_MISS_sum"] > 0:
+        out.append(("l2_hit_fraction", f"{m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}"))
+    if "TCP_UTCL1_TRANSLATION_MISS_sum" in m and "TCP_UTCL1_TRANSLATION_HIT_sum" in m:
+        tot = m["TCP_UTCL1_TRANSLATION_MISS_sum"] + m["TCP_UTCL1_TRANSLATION_HIT_sum"]
+        if tot > 0:
+            out.append(("utcl1_translation_miss_fraction",
+                        f"{m['TCP_UTCL1_TRANSLATION_MISS_sum'] / tot:.4f}"))
+    return out
 
 
 if __name__ == "__main__":
