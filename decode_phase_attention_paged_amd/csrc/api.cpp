@@ -7,6 +7,7 @@
 #include <climits>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "decode_attn.h"
 #include "kernels.h"
@@ -38,6 +39,9 @@ std::mutex g_mutex;
 int g_cus[kMaxDevices];            // compute units per device, 0 = not queried yet
 void* g_ws[kMaxDevices];           // library-owned workspace per device
 size_t g_ws_bytes[kMaxDevices];
+// Buffers a larger call superseded. They are never freed: work still queued, or a HIP
+// graph captured from an earlier call, may read them at any later time.
+std::vector<void*> g_ws_retired[kMaxDevices];
 
 int current_device_cus(int* cus) {
   int dev = 0;
@@ -331,15 +335,11 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages, const f
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DECODE_ATTN_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mutex);
     if (g_ws_bytes[dev] < need) {
-      if (g_ws[dev] != nullptr) {
-        // Work already queued may still read the old buffer.
-        if (hipDeviceSynchronize() != hipSuccess) return DECODE_ATTN_ERR_HIP;
-        (void)hipFree(g_ws[dev]);
-        g_ws[dev] = nullptr;
-        g_ws_bytes[dev] = 0;
-      }
       void* p = nullptr;
       if (hipMalloc(&p, need) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+      // The old buffer stays allocated: queued work and graphs captured from earlier
+      // calls keep its address.
+      if (g_ws[dev] != nullptr) g_ws_retired[dev].push_back(g_ws[dev]);
       g_ws[dev] = p;
       g_ws_bytes[dev] = need;
     }

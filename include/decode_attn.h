@@ -129,12 +129,13 @@ typedef struct {
  * num_pages >= 1 is the number of pages in each pool, used only to reject bad table
  * entries on the device; scale is the softmax scale (typically 1/sqrt(head_dim)).
  * The plan is the library's choice for the current device (decode_attn_plan with no
- * request), and the library uses a workspace it owns: one buffer per device, grown with
- * hipMalloc on demand and kept until the process ends. This entry point therefore may
- * allocate (on its first call for a shape; capture it in a HIP graph only after such a
- * call), and two calls that overlap on one device
- * (different streams or host threads) must not share that workspace; such callers use
- * decode_attn_ex. Returns a decode_attn_status.
+ * request), and the library uses a workspace it owns: one buffer per device, replaced by
+ * a larger one (hipMalloc) when a call needs more. A replaced buffer is never freed: it
+ * stays allocated until the process ends, so work already queued and HIP graphs captured
+ * from earlier calls keep valid addresses. This entry point therefore may allocate (on
+ * its first call for a larger shape; capture it in a HIP graph only after such a call),
+ * and two calls that overlap on one device (different streams or host threads) must not
+ * share that workspace; such callers use decode_attn_ex. Returns a decode_attn_status.
  */
 int decode_attn(const void* q, const void* k_pages, const void* v_pages,
                 const float* k_scale, const float* v_scale,

@@ -175,3 +175,61 @@ def test_split_workspace_serves_many_calls(torch, lib, kv):
         call(lib, d, w, out, ws, num_splits=splits)
         torch.cuda.synchronize()
         assert_parity(out.cpu().numpy(), oracle_run(w)[0], f"call {i} splits {splits}")
+
+
+def test_library_workspace_growth_keeps_earlier_graphs_valid(torch, lib):
+    # decode_attn owns its workspace and replaces it by a larger buffer when a call needs
+    # more. A graph captured from an earlier, smaller call keeps the old buffer's address,
+    # so that buffer must stay allocated: capture a small split-mode call, grow the
+    # workspace with an eager stream-mode call over a 64/8-head batch (the largest
+    # workspace the library's plans use), allocate and scribble over fresh memory, then
+    # replay the small graph.
+    small = SMALL.with_(len_hi=700)
+    w = generate(small, seed=95)
+    d = to_dev(torch, w)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = lib.plan(small.batch, small.max_blocks_per_seq, small.n_q_heads, small.n_kv_heads, 16,
+                 "fp16", num_cus=cus)
+    assert p.mode == lib.MODE_SPLIT and p.workspace_bytes > 0
+    out = torch.zeros(w.q.shape, dtype=torch.float32, device="cuda:0")
+    print("case workspace growth: small split call", flush=True)
+
+    def small_call():
+        lib.decode_attn(d["q"], d["k_pages"], d["v_pages"], d["block_table"], d["seq_lens"],
+                        w.scale, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        small_call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        small_call()
+    torch.cuda.synchronize()
+
+    big = Config(0, "g8_stream", batch=40, n_q_heads=64, n_kv_heads=8, head_dim=128,
+                 block_size=16, len_lo=1100, len_hi=2000, kv_dtype="fp16")
+    bp = lib.plan(big.batch, big.max_blocks_per_seq, big.n_q_heads, big.n_kv_heads, 16, "fp16",
+                  num_cus=cus)
+    assert bp.mode == lib.MODE_STREAM and bp.workspace_bytes > p.workspace_bytes
+    wb = generate(big, seed=96)
+    db = to_dev(torch, wb)
+    print("case workspace growth: large stream call", flush=True)
+    big_out = lib.decode_attn(db["q"], db["k_pages"], db["v_pages"], db["block_table"],
+                              db["seq_lens"], wb.scale)
+    torch.cuda.synchronize()
+    assert_parity(big_out.cpu().numpy(), oracle_run(wb)[0], "large call that grew the workspace")
+    junk = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(97)
+    for replay in range(2):
+        q_new = rng.standard_normal(w.q.shape).astype(np.float16)
+        d["q"].copy_(dev_tensor(torch, q_new))
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        w.q = q_new
+        assert_parity(out.cpu().numpy(), oracle_run(w)[0], f"small graph replay {replay} after growth")
+    del junk
