@@ -54,7 +54,8 @@ def _row_dtype(kv):
     return torch.bfloat16 if kv == KV_BF16 else torch.float16
 STATUS = {0: "DECODE_ATTN_OK", 1: "DECODE_ATTN_ERR_INVALID_ARGUMENT",
           2: "DECODE_ATTN_ERR_UNSUPPORTED", 3: "DECODE_ATTN_ERR_WORKSPACE",
-          4: "DECODE_ATTN_ERR_HIP"}
+          4: "DECODE_ATTN_ERR_HIP", 5: "DECODE_ATTN_ERR_SCRATCH_LIMIT"}
+STATIC_SCRATCH_BYTES = 32 << 20   # DECODE_ATTN_STATIC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -83,6 +84,8 @@ _SIGNATURES = {
     "decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P]),
     "decode_attn_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P,
                             _P, _I, _I, _P, _SZ, _P]),
+    "decode_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                                 _P, _P, _I, _I, _P]),
     "decode_attn_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "decode_attn_append": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "decode_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -242,6 +245,30 @@ def decode_attn_ex(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale
                                 num_workgroups, num_splits, _ptr(workspace), ws_bytes,
                                 _stream(q.device))
     _check(st, "decode_attn_ex")
+    return out
+
+
+def decode_attn_noalloc(q, k_pages, v_pages, block_table, seq_lens, scale, *, k_scale=None,
+                        v_scale=None, out, lse_out=None, num_workgroups=0, num_splits=0):
+    """decode_attn_ex without a workspace argument: the library's static per-device
+    scratch array serves as the workspace, and nothing is allocated (``out`` must be
+    given). Plans needing more than STATIC_SCRATCH_BYTES of workspace raise
+    DECODE_ATTN_ERR_SCRATCH_LIMIT. Calls that overlap on one device share the array and
+    must not run concurrently. Returns ``out``."""
+    lib = load_library()
+    kv, batch, mb, np_, n_q, n_kv, d, bs = _common(q, k_pages, v_pages, block_table, seq_lens,
+                                                   k_scale, v_scale, out)
+    if lse_out is not None:
+        if (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (batch, n_q)
+                or not lse_out.is_contiguous() or lse_out.device != q.device):
+            raise ValueError("lse_out must be contiguous fp32 [batch, n_q_heads] on q's device")
+    with torch.cuda.device(q.device):
+        st = lib.decode_attn_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale),
+                                     _ptr(v_scale), _ptr(block_table), _ptr(seq_lens), batch, mb,
+                                     np_, n_q, n_kv, d, bs, kv, float(scale), _ptr(out),
+                                     _ptr(lse_out), num_workgroups, num_splits,
+                                     _stream(q.device))
+    _check(st, "decode_attn_noalloc")
     return out
 
 

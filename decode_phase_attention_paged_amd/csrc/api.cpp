@@ -17,7 +17,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (6 << 16) | 2;
+constexpr int kVersion = (6 << 16) | 3;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -311,6 +311,38 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages, cons
              plan, need > 0 ? workspace : nullptr, stream);
 }
 
+int decode_attn_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                        const float* k_scale, const float* v_scale, const int32_t* block_table,
+                        const int32_t* seq_lens, int batch, int max_blocks_per_seq, int num_pages,
+                        int n_q_heads, int n_kv_heads, int head_dim, int block_size, int kv_dtype,
+                        float scale, float* out, float* lse_out, int requested_workgroups,
+                        int requested_splits, hipStream_t stream) {
+  int st = validate(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, batch,
+                    max_blocks_per_seq, num_pages, n_q_heads, n_kv_heads, head_dim, block_size,
+                    kv_dtype, out, lse_out, requested_workgroups, requested_splits);
+  if (st != DECODE_ATTN_OK) return st;
+  if (batch == 0) return DECODE_ATTN_OK;
+  int cus = 0;
+  if (plan_needs_cus(max_blocks_per_seq, requested_workgroups, requested_splits)) {
+    st = current_device_cus(&cus);
+    if (st != DECODE_ATTN_OK) return st;
+  }
+  const dattn::Plan plan = make_plan(batch, max_blocks_per_seq, n_kv_heads, kv_of(kv_dtype),
+                                     n_q_heads / n_kv_heads, requested_workgroups,
+                                     requested_splits, cus);
+  st = validate_plan(plan, batch);
+  if (st != DECODE_ATTN_OK) return st;
+  const size_t need = dattn::workspace_bytes(plan, batch, n_q_heads, n_kv_heads);
+  if (need > dattn::kStaticScratchBytes) return DECODE_ATTN_ERR_SCRATCH_LIMIT;
+  // The device's static scratch array (its address is looked up on the first call that
+  // gets here on each device); no allocation of any kind.
+  void* ws = nullptr;
+  if (dattn::static_scratch(&ws) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  return run(q, k_pages, v_pages, k_scale, v_scale, block_table, seq_lens, batch,
+             max_blocks_per_seq, num_pages, n_q_heads, n_kv_heads, kv_dtype, scale, out, lse_out,
+             plan, need > 0 ? ws : nullptr, stream);
+}
+
 int decode_attn(const void* q, const void* k_pages, const void* v_pages, const float* k_scale,
                 const float* v_scale, const int32_t* block_table, const int32_t* seq_lens,
                 int batch, int max_blocks_per_seq, int num_pages, int n_q_heads, int n_kv_heads,
@@ -456,6 +488,7 @@ const char* decode_attn_status_string(int status) {
     case DECODE_ATTN_ERR_UNSUPPORTED: return "DECODE_ATTN_ERR_UNSUPPORTED";
     case DECODE_ATTN_ERR_WORKSPACE: return "DECODE_ATTN_ERR_WORKSPACE";
     case DECODE_ATTN_ERR_HIP: return "DECODE_ATTN_ERR_HIP";
+    case DECODE_ATTN_ERR_SCRATCH_LIMIT: return "DECODE_ATTN_ERR_SCRATCH_LIMIT";
     default: return "DECODE_ATTN_UNKNOWN_STATUS";
   }
 }

@@ -90,6 +90,12 @@ void bind_workspace(Args& a, const Plan& plan, void* workspace);
 // Enqueue the main kernel and the merge of the partial results it leaves.
 hipError_t launch(KvType kv, int group, const Args& a, const Plan& plan, hipStream_t stream);
 
+// Workspace that lives in the code object, for calls that must not allocate: a static
+// device array of kStaticScratchBytes per device. static_scratch gives the current
+// device's copy (its address is looked up once per device and kept).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Appending a decode step's new K/V rows to the paged cache (append.hip).
 struct AppendArgs {
   const void* k_new;           // fp16 [B, Hkv, D] (bf16 for a bf16 cache)

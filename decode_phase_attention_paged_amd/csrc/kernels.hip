@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kernels.h"
@@ -1430,6 +1431,34 @@ hipError_t launch_kv(int group, const Args& a, const Plan& plan, hipStream_t str
 constexpr size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 }  // namespace
+
+// The no-allocation entry point's workspace: one array per device, alive until the process
+// ends. Host code never passes `scratch` itself to a kernel (on the host it is only a
+// stand-in for the symbol); it passes the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices];   // device address of `scratch`, per device
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t workspace_bytes(const Plan& plan, int batch, int n_q_heads, int n_kv_heads) {
   const size_t group = static_cast<size_t>(n_q_heads / n_kv_heads);

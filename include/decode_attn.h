@@ -93,8 +93,13 @@ typedef enum {
                                            scales given for FP16 or missing for INT8 */
   DECODE_ATTN_ERR_UNSUPPORTED = 2,      /* a size this build has no kernel for */
   DECODE_ATTN_ERR_WORKSPACE = 3,        /* workspace missing or too small */
-  DECODE_ATTN_ERR_HIP = 4               /* a HIP call or kernel launch failed */
+  DECODE_ATTN_ERR_HIP = 4,              /* a HIP call or kernel launch failed */
+  DECODE_ATTN_ERR_SCRATCH_LIMIT = 5     /* decode_attn_noalloc: the plan needs more workspace
+                                           than DECODE_ATTN_STATIC_SCRATCH_BYTES */
 } decode_attn_status;
+
+/* Size of the device-resident workspace decode_attn_noalloc uses: 32 MiB per device. */
+#define DECODE_ATTN_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Storage type of k_pages / v_pages. */
 typedef enum {
@@ -189,6 +194,29 @@ int decode_attn_ex(const void* q, const void* k_pages, const void* v_pages,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * decode_attn_ex for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, and harnesses that forbid hipMalloc. It takes the same arguments minus
+ * the workspace and never allocates (no hipMalloc, hipFree or allocating library call):
+ * the plan's workspace is a static device array of DECODE_ATTN_STATIC_SCRATCH_BYTES
+ * (32 MiB) in the library's code object, one per device, held until the process ends. Its
+ * device address is looked up (hipGetSymbolAddress) on the first call on each device, with
+ * that device current. A plan whose workspace_bytes (see decode_attn_plan) exceeds the
+ * limit returns DECODE_ATTN_ERR_SCRATCH_LIMIT before any HIP call; segment-mode plans need
+ * none. Every call on one device shares that device's array and leaves its contents behind
+ * (nothing in it has to start at zero: each call writes every entry it later reads), so
+ * calls that overlap on one device (different streams or host threads) race and must be
+ * serialised by the caller. Results are bitwise those of decode_attn_ex with the same
+ * requests. Returns a decode_attn_status.
+ */
+int decode_attn_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int batch, int max_blocks_per_seq, int num_pages,
+                        int n_q_heads, int n_kv_heads, int head_dim, int block_size,
+                        int kv_dtype, float scale, float* out, float* lse_out,
+                        int requested_workgroups, int requested_splits, hipStream_t stream);
+
+/*
  * Append a decode step's new key and value rows to the paged cache: every decode step
  * adds the new token's K and V before attending (page "Eine LLM-Inferenz-Engine von
  * Grund auf mit C++ und CUDA bauen", section 1.1), and token position p of sequence b
@@ -274,7 +302,8 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
 const char* decode_attn_status_string(int status);
 
 /* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats;
-   6.1 adds decode_attn_prefill; 6.2 gives it every storage format (row scale arguments). */
+   6.1 adds decode_attn_prefill; 6.2 gives it every storage format (row scale arguments);
+   6.3 adds decode_attn_noalloc. */
 int decode_attn_version(void);
 
 #ifdef __cplusplus

@@ -34,8 +34,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_plan",
-        "decode_attn_prefill", "decode_attn_status_string", "decode_attn_version"])
+        "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_noalloc",
+        "decode_attn_plan", "decode_attn_prefill", "decode_attn_status_string",
+        "decode_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -51,11 +52,11 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 2
-    names = [lib.decode_attn_status_string(i).decode() for i in range(5)]
+    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 3
+    names = [lib.decode_attn_status_string(i).decode() for i in range(6)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
-                     "DECODE_ATTN_ERR_HIP"]
+                     "DECODE_ATTN_ERR_HIP", "DECODE_ATTN_ERR_SCRATCH_LIMIT"]
     assert lib.decode_attn_status_string(99) == b"DECODE_ATTN_UNKNOWN_STATUS"
 
 
@@ -143,6 +144,28 @@ def test_explicit_plans_need_no_device_and_check_the_workspace(lib, binding):
     g = plan(lib, binding, 2, 8, 8, 2, wgs=7, splits=1)
     assert (g.mode, g.num_workgroups, g.num_splits, g.pages_per_split, g.workspace_bytes) == (
         binding.MODE_SEGMENT, 7, 1, 0, 0)
+
+
+def call_noalloc(lib, wgs, splits, **over):
+    a = dict(GOOD, **over)
+    return lib.decode_attn_noalloc(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["sl"],
+                                   a["batch"], a["mb"], a["np_"], a["hq"], a["hkv"], a["d"],
+                                   a["bs"], a["kv"], a["scale"], a["out"], None, wgs, splits,
+                                   None)
+
+
+def test_noalloc_checks_arguments_and_its_scratch_limit_before_any_hip_call(lib, binding):
+    # Stream mode on 20000 workgroups needs 80000 workers x 2 slots x G = 4 rows of 129
+    # floats, far beyond the 32 MiB static scratch array; 4 workgroups fit.
+    assert binding.STATIC_SCRATCH_BYTES == 32 << 20
+    assert plan(lib, binding, 2, 8, 8, 2, wgs=20000).workspace_bytes > binding.STATIC_SCRATCH_BYTES
+    assert plan(lib, binding, 2, 8, 8, 2, wgs=4).workspace_bytes < binding.STATIC_SCRATCH_BYTES
+    assert call_noalloc(lib, 20000, 0) == 5
+    assert call_noalloc(lib, 20000, 0, hq=6, hkv=4) == 1     # arguments are checked first
+    assert call_noalloc(lib, 4, 3) == 1                      # a grid with several partitions
+    assert call_noalloc(lib, 4, 0, d=64) == 2
+    assert call_noalloc(lib, 4, 0, batch=0, q=None, k=None, v=None, bt=None, sl=None,
+                        out=None) == 0                       # empty batch: nothing enqueued
 
 
 def test_stream_mode_refuses_batches_beyond_the_lds_scan(lib, binding):
