@@ -12,7 +12,8 @@ serving the KV reads, the step rotates over R replicas of the page pools totalli
 least 1 GiB. Throughput counts algorithmic KV bytes only: sum_b L_b * Hkv * 2 * D * elem
 (plus the fp32 row scales for INT8 and FP8).
 
-Timing: W warm-up steps, then `repeats` windows of exactly --steps back-to-back steps,
+Timing: W warm-up steps (continued until at least 0.25 s of GPU work has run, so that the
+clocks are up), then `repeats` windows of exactly --steps back-to-back steps,
 each between one pair of HIP events on the launch stream with a device synchronisation
 on both sides. `value` and `us_per_step` are the median window; the spread is reported.
 
@@ -369,9 +370,7 @@ def main():
 
     log(f"plan: {plan} replicas={reps} "
         f"pool={pool_bytes / 1e6:.1f} MB kv_bytes/step={w.kv_bytes / 1e6:.1f} MB")
-    for i in range(args.warmup):
-        rotate(i)
-    torch.cuda.synchronize()
+    args.warmup_run = warm_up(torch, rotate, args.warmup)
 
     step = rotate
     if args.graph > 0:
@@ -397,7 +396,7 @@ def main():
         steps_per_window, scale_steps = args.steps, 1
 
     total_ms, walls = timed_windows(torch, stream, step, steps_per_window, args.repeats,
-                                    args.warmup)
+                                    args.warmup_run)
     st = window_stats(total_ms, steps_per_window * scale_steps)
     ms_per_step = st["median_ms"]
     gbs = w.kv_bytes / (ms_per_step / 1e3) / 1e9
@@ -409,8 +408,7 @@ def main():
 
     hot_rec = None
     if not args.no_hot and args.graph == 0:
-        for i in range(args.warmup):
-            hot(i)
+        warm_up(torch, hot, args.warmup)
         hot_ms, _ = timed_windows(torch, stream, hot, args.steps, args.repeats, 0)
         hs = window_stats(hot_ms, args.steps)
         hot_rec = {"us_per_step": round(hs["median_ms"] * 1e3, 3),
@@ -441,6 +439,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": getattr(args, "warmup_run", args.warmup),
         "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
@@ -534,12 +533,31 @@ def grow_for_append(w, np, cfg):
     return table, positions, fresh
 
 
+MIN_WARMUP_S = 0.25
+
+
+def warm_up(torch, step, warmup: int) -> int:
+    """`warmup` untimed steps, then more until at least MIN_WARMUP_S of GPU work has run:
+    after the host-side data generation the GPU has idled for seconds, and its clocks take
+    tens of milliseconds of load to come back up. Returns the number of steps run."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup:
+        step(i)
+        i += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        for _ in range(16):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
 def timed_record(args, torch, stream, step, nbytes):
     """Warm-up, then the timed windows; returns (median ms/step, stats)."""
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    total_ms, _ = timed_windows(torch, stream, step, args.steps, args.repeats, args.warmup)
+    args.warmup_run = warm_up(torch, step, args.warmup)
+    total_ms, _ = timed_windows(torch, stream, step, args.steps, args.repeats, args.warmup_run)
     st = window_stats(total_ms, args.steps)
     return st["median_ms"], st
 
@@ -617,6 +635,7 @@ def bench_append(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": getattr(args, "warmup_run", args.warmup),
         "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
@@ -705,6 +724,7 @@ def bench_step(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": getattr(args, "warmup_run", args.warmup),
         "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),
@@ -813,6 +833,7 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": getattr(args, "warmup_run", args.warmup),
         "repeats": args.repeats,
         "ms_per_step": round(ms_per_step, 6),
         "us_per_step": round(ms_per_step * 1e3, 3),

@@ -37,7 +37,7 @@ constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 
 // Waves per SIMD the segment-mode kernel is compiled for, by element width (2-byte and
 // 1-byte formats) and log2 G; the host sizes that mode's grid to the workgroups that stay
 // resident at that occupancy.
-constexpr int kSegWavesF16[4] = {3, 2, 2, 1};
+constexpr int kSegWavesF16[4] = {1, 2, 1, 1};
 constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
 constexpr int seg_waves(KvType kv, int group) {
   return kv_elem_bytes(kv) == 2 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];

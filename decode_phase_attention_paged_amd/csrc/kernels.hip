@@ -894,6 +894,20 @@ struct SegList {
   }
 };
 
+// Workgroups are dispatched to the 8 XCDs round robin (workgroup w runs on XCD w mod 8),
+// and each XCD has its own L2. The snake deal gives list positions 2m and 2m + 1 (the same
+// sequence, KV heads 2j and 2j + 1) to the logical workgroups of one pair {2i, 2i + 1}. This
+// map from a launched workgroup to its logical index places both of a pair on one XCD
+// (launched workgroups 16c + x and 16c + 8 + x), so the 128-byte lines that hold two heads'
+// row scales (64 bytes each) are fetched from HBM once and then hit in that XCD's L2.
+// A grid that is not a multiple of 16 keeps the plain order in its last partial block.
+constexpr bool kPairHeadsOnXcd = true;
+__device__ __forceinline__ uint32_t logical_workgroup(uint32_t w, uint32_t grid) {
+  if (!kPairHeadsOnXcd || w >= (grid & ~15u)) return w;
+  const uint32_t j = w & 15u;
+  return (w & ~15u) + 2u * (j & 7u) + (j >> 3);
+}
+
 // One unit of a wave's run, all in scalar registers.
 struct SegRec {
   uint32_t tile;   // phys * Hkv + g (0 when the page id failed the range check)
@@ -930,7 +944,7 @@ void seg_kernel(Args a) {
   const uint32_t mb = static_cast<uint32_t>(a.max_blocks);
 
   SegList L;
-  L.w = blockIdx.x;
+  L.w = logical_workgroup(blockIdx.x, gridDim.x);
   L.P = gridDim.x;
   L.hkv = hkv;
   L.max_tokens = a.max_blocks * kBlockSize;
@@ -951,21 +965,25 @@ void seg_kernel(Args a) {
   //    (empty and invalid lengths count as 0, so they come last). In index order nothing
   //    has to be read before the first loads below: lengths come through scalar loads.
   if (L.ordered) {
-    int key = -1;   // pads past the batch: below every real key
+    // The order is by decreasing length, ties by index, with lengths clamped to 2^24 - 1
+    // (longer caches tie). Length and index fold into one unsigned key,
+    // (length << 8) | (255 - index), so that the rank is one comparison per sequence; the
+    // pads past the batch are 0, below every real key.
+    uint32_t key = 0;
     if (tid < batch) {
       const int len = a.seq_lens[tid];
       s_len[tid] = static_cast<uint32_t>(len);
-      key = len > 0 && len <= L.max_tokens ? len : 0;
+      const uint32_t valid = len > 0 && len <= L.max_tokens ? static_cast<uint32_t>(len) : 0u;
+      key = (min(valid, (1u << 24) - 1u) << 8) | static_cast<uint32_t>(kOrderMax - 1 - tid);
     }
-    if (tid < kOrderMax) reinterpret_cast<int*>(s_key)[tid] = key;
+    if (tid < kOrderMax) reinterpret_cast<uint32_t*>(s_key)[tid] = key;
     __syncthreads();
     if (tid < batch) {
-      int rank = 0;
+      uint32_t rank = 0;
       for (int u4 = 0; u4 < (batch + 3) / 4; ++u4) {
-        const int4 k = s_key[u4];
-        const int u = 4 * u4;
-        rank += (k.x > key || (k.x == key && u < tid)) + (k.y > key || (k.y == key && u + 1 < tid)) +
-                (k.z > key || (k.z == key && u + 2 < tid)) + (k.w > key || (k.w == key && u + 3 < tid));
+        const u32x4 k = reinterpret_cast<const u32x4*>(s_key)[u4];
+        rank += static_cast<uint32_t>(k[0] > key) + static_cast<uint32_t>(k[1] > key) +
+                static_cast<uint32_t>(k[2] > key) + static_cast<uint32_t>(k[3] > key);
       }
       s_order[rank] = static_cast<uint32_t>(tid);
     }
@@ -1003,9 +1021,6 @@ void seg_kernel(Args a) {
     stage_load(k0);
     stage_store(k0);
   };
-  // The first chunk's loads are issued now and stored to LDS only after the first tile
-  // loads below have been issued, so their latencies overlap.
-  stage_load(0);
 
   QRegs<kKv, kGroup> qh;
   auto load_q = [&](uint32_t k) __attribute__((always_inline)) {
@@ -1038,13 +1053,15 @@ void seg_kernel(Args a) {
     }
   };
   // The first segment's length and this wave's first page id in it are loaded together
-  // (the page id speculatively: table entries below max_blocks are always in bounds).
+  // (the page id speculatively: table entries below max_blocks are always in bounds), and
+  // its query rows go straight to registers, ahead of the first tile loads.
   int32_t phys_next = 0;
   {
     uint32_t b0, g0;
     L.head_of<true>(0, b0, g0);
     const int32_t first_page =
         static_cast<uint32_t>(wave) < mb ? scalar_load(a.block_table, static_cast<size_t>(b0) * mb + wave) : 0;
+    load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(b0 * hkv + g0) * kQRow16 * 16, col);
     seek();
     if (ck < L.n)
       phys_next = ck == 0 ? first_page : scalar_load(a.block_table, static_cast<size_t>(cb) * mb + cj);
@@ -1082,12 +1099,13 @@ void seg_kernel(Args a) {
     rec[d] = take();
     load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
   });
-  stage_store(0);
-  __syncthreads();
+  // The first chunk of query rows goes to LDS only now, behind the first tile loads: the
+  // first segment's rows are already on their way to registers.
+  stage_load(0);
+  stage_store(0);   // read only after the barrier of the first segment's end
 
   State<kKv, kGroup> st;
   reset(st);
-  load_q(0);
   bool seg_bad = false;
   uint32_t cur = 0;   // segment whose state st holds
 

@@ -202,22 +202,24 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     p3 = plan(lib, binding, 160, 256, 32, 8)
     p4 = plan(lib, binding, 1, 8192, 32, 8)
     p5 = plan(lib, binding, 200, 34, 32, 32, kv=1)
-    # Many (sequence, head) pairs over short caches: segment mode, as many workgroups as
-    # stay resident (three per compute unit), no workspace.
-    for p in (p2, p5):
-        assert (p.mode, p.num_splits, p.num_workgroups) == (binding.MODE_SEGMENT, 1, 768)
-        assert p.workspace_bytes == 0
+    # Many (sequence, head) pairs over short caches: segment mode, one workgroup per
+    # compute unit for 16-bit caches with G = 1 and three for INT8 (the workgroups resident
+    # at each build's occupancy), no workspace.
+    assert (p2.mode, p2.num_splits, p2.num_workgroups) == (binding.MODE_SEGMENT, 1, 256)
+    assert (p5.mode, p5.num_splits, p5.num_workgroups) == (binding.MODE_SEGMENT, 1, 768)
+    assert p2.workspace_bytes == 0 and p5.workspace_bytes == 0
     # Never more workgroups than segments; the INT8 build for G = 8 spills, so it stays in
     # stream mode.
-    assert plan(lib, binding, 3, 8, 1, 1, cus=2).num_workgroups == 3
-    assert plan(lib, binding, 3, 8, 8, 8, cus=2).num_workgroups == 6
+    assert plan(lib, binding, 3, 8, 1, 1, cus=4).num_workgroups == 3
+    assert plan(lib, binding, 3, 8, 8, 8, cus=30).num_workgroups == 24
+    assert plan(lib, binding, 3, 8, 8, 8, cus=20).num_workgroups == 20
     assert plan(lib, binding, 300, 8, 8, 1, cus=2).mode == binding.MODE_SEGMENT
     assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=1).mode == binding.MODE_STREAM
     assert plan(lib, binding, 300, 8, 8, 4, cus=2).mode == binding.MODE_SEGMENT
     # Many pairs over long caches: segment mode while every workgroup gets two segments or
-    # more (1280 pairs, 512 workgroups for G = 4), else the balanced stream.
-    assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 512
-    s3 = plan(lib, binding, 100, 256, 32, 8)
+    # more (1280 pairs, 256 workgroups for G = 4), else the balanced stream.
+    assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 256
+    s3 = plan(lib, binding, 60, 256, 32, 8)
     assert s3.mode == binding.MODE_STREAM and s3.num_workgroups == 512
     # Few long caches: split mode, about one workgroup per CU.
     assert (p4.mode, p4.num_splits, p4.pages_per_split, p4.num_workgroups) == (
@@ -228,7 +230,7 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     assert plan(lib, binding, 1, 1, 8, 8).mode == binding.MODE_SEGMENT
     p17 = plan(lib, binding, 1, 17, 8, 8)
     assert p17.mode == binding.MODE_SPLIT and p17.num_splits == 17
-    assert plan(lib, binding, 160, 256, 32, 8, cus=80).num_workgroups == 160
+    assert plan(lib, binding, 160, 256, 32, 8, cus=80).num_workgroups == 80
 
 
 def test_plan_rejects_bad_arguments(lib, binding):

@@ -171,6 +171,22 @@ def test_segment_mode_order_and_grids(torch, lib, batch, grid, caches):
     assert_lse(lse, ref_lse, "lse")
 
 
+@pytest.mark.parametrize("grid", [1, 2, 3])
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_segment_mode_very_long_segments(torch, lib, grid, kv):
+    # Segment mode over caches of 4096, 4097, 4375 and 8750 pages, with short and empty
+    # caches between; on one workgroup they all run back to back.
+    lens = np.array([140000, 65536, 100, 65537, 0, 70000, 17], dtype=np.int32)
+    cfg = SMALL.with_(kv_dtype=kv, batch=len(lens), n_q_heads=4, n_kv_heads=2, len_lo=0,
+                      len_hi=int(lens.max()))
+    w = generate(cfg, seed=62, seq_lens=lens, poison=True, extra_pages=3)
+    print(f"case segment chunks kv={kv} grid={grid}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w, num_splits=1, num_workgroups=grid)
+    assert_parity(got, ref, f"segment chunks {kv} grid {grid}")
+    assert_lse(lse, ref_lse, "lse")
+
+
 @pytest.mark.parametrize("kv", KVS)
 def test_stream_mode_query_rows_beyond_lds(torch, lib, kv):
     # Stream mode stages a workgroup's query rows in LDS when they fit in 16 KiB; one
