@@ -48,6 +48,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
 METRIC = "decode-attn KV-read GB/s (fraction of MI355X HBM peak) + µs/step"
 PROFILES = os.path.join(ROOT, "profiles")
 DEFAULT_CONFIG = {"attn": 3, "append": 2, "step": 2, "prefill": 8}
+MIN_WARMUP_S = 0.25   # least GPU work before the timed windows (clocks up after idling)
 
 
 def log(msg):
@@ -268,6 +269,8 @@ def main():
                     help="1 = segment mode, >1 = split mode with this many partitions "
                          "(0 = the library's plan)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB")
+    ap.add_argument("--min-warmup-s", type=float, default=MIN_WARMUP_S,
+                    help="keep warming up until this much GPU work has run (0 for profiled runs)")
     ap.add_argument("--no-hot", action="store_true",
                     help="skip the labelled one-replica (hot pool) figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -370,7 +373,7 @@ def main():
 
     log(f"plan: {plan} replicas={reps} "
         f"pool={pool_bytes / 1e6:.1f} MB kv_bytes/step={w.kv_bytes / 1e6:.1f} MB")
-    args.warmup_run = warm_up(torch, rotate, args.warmup)
+    args.warmup_run = warm_up(torch, rotate, args.warmup, args.min_warmup_s)
 
     step = rotate
     if args.graph > 0:
@@ -408,7 +411,7 @@ def main():
 
     hot_rec = None
     if not args.no_hot and args.graph == 0:
-        warm_up(torch, hot, args.warmup)
+        warm_up(torch, hot, args.warmup, args.min_warmup_s)
         hot_ms, _ = timed_windows(torch, stream, hot, args.steps, args.repeats, 0)
         hs = window_stats(hot_ms, args.steps)
         hot_rec = {"us_per_step": round(hs["median_ms"] * 1e3, 3),
@@ -533,20 +536,17 @@ def grow_for_append(w, np, cfg):
     return table, positions, fresh
 
 
-MIN_WARMUP_S = 0.25
-
-
-def warm_up(torch, step, warmup: int) -> int:
-    """`warmup` untimed steps, then more until at least MIN_WARMUP_S of GPU work has run:
+def warm_up(torch, step, warmup: int, min_s: float = MIN_WARMUP_S) -> int:
+    """`warmup` untimed steps, then more until at least `min_s` seconds of GPU work have run:
     after the host-side data generation the GPU has idled for seconds, and its clocks take
-    tens of milliseconds of load to come back up. Returns the number of steps run."""
+    tens of milliseconds of load to come back up. Returns the number of steps run.""" 
     t0 = time.perf_counter()
     i = 0
     while i < warmup:
         step(i)
         i += 1
     torch.cuda.synchronize()
-    while time.perf_counter() - t0 < MIN_WARMUP_S:
+    while time.perf_counter() - t0 < min_s:
         for _ in range(16):
             step(i)
             i += 1
@@ -556,7 +556,7 @@ def warm_up(torch, step, warmup: int) -> int:
 
 def timed_record(args, torch, stream, step, nbytes):
     """Warm-up, then the timed windows; returns (median ms/step, stats)."""
-    args.warmup_run = warm_up(torch, step, args.warmup)
+    args.warmup_run = warm_up(torch, step, args.warmup, args.min_warmup_s)
     total_ms, _ = timed_windows(torch, stream, step, args.steps, args.repeats, args.warmup_run)
     st = window_stats(total_ms, args.steps)
     return st["median_ms"], st
@@ -877,7 +877,7 @@ COUNTER_PASSES = {
              "GRBM_GUI_ACTIVE"],
     "sq_b": ["SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_INSTS_SMEM",
              "SQ_ACTIVE_INST_VMEM", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_INSTS_VMEM",
-             "GRBM_GUI_ACTIVE"],
+             "GRBM_GUI_ACTIVE"],   # SQ_ACTIVE_INST_VMEM reads 0 on gfx950
     "mem": ["TCC_HIT_sum", "TCC_MISS_sum", "TCP_UTCL1_TRANSLATION_MISS_sum",
             "TCP_UTCL1_TRANSLATION_HIT_sum", "TCP_TCC_READ_REQ_sum"],
 }
@@ -1049,17 +1049,13 @@ def derived_counters(ctr, kernel_ns):
     gui = m.get("GRBM_GUI_ACTIVE")
     if gui:
         cycles = gui / N_XCD
-        out.append(("gpu_busy_cycles", f"{cycles:.0f}  ({cycles / kernel_ns:.2f} per ns of the "
-                                       f"traced kernel time)"))
+        out.append(("gpu_busy_cycles_of_the_profiled_dispatch", f"{cycles:.0f}"))
         if "SQ_WAVE_CYCLES" in m:
             out.append(("mean_resident_waves_per_cu",
                         f"{4 * m['SQ_WAVE_CYCLES'] / (cycles * N_CU):.2f}"))
         if "SQ_ACTIVE_INST_VALU" in m:
             out.append(("valu_busy_fraction_per_simd",
                         f"{4 * m['SQ_ACTIVE_INST_VALU'] / (cycles * N_SIMD):.3f}"))
-        if "SQ_ACTIVE_INST_VMEM" in m:
-            out.append(("vmem_issue_fraction_per_simd",
-                        f"{4 * m['SQ_ACTIVE_INST_VMEM'] / (cycles * N_SIMD):.3f}"))
         if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
             out.append(("mfma_busy_fraction_per_simd",
                         f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * N_SIMD):.3f}"))
