@@ -10,6 +10,7 @@ hipStream_t handles are valid inside it.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -51,9 +52,31 @@ def compile_cmd(out: str = LIB_PATH, extra=()) -> list:
 
 def _filter_stderr(text: str) -> str:
     # hipcc's host pass does not know the packed-fp32 feature name; that warning is
-    # expected. Anything else is shown.
-    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    # expected, and the kernel resource remarks are read by scratch_use(). Anything else is
+    # shown.
+    lines = [ln for ln in text.splitlines()
+             if "packed-fp32-ops" not in ln and "kernel-resource-usage" not in ln]
     return "\n".join(lines) + "\n" if any(ln.strip() for ln in lines) else ""
+
+
+# Every kernel is built to keep its live values in registers: a build that spills to
+# scratch memory runs several times slower, so the build fails if any kernel reports
+# scratch. The compiler's resource remarks name each kernel and its scratch bytes per lane.
+RESOURCE_FLAGS = ["-Rpass-analysis=kernel-resource-usage", "-fno-caret-diagnostics"]
+
+
+def scratch_use(remarks: str) -> dict:
+    """{kernel symbol: scratch bytes per lane} from the compiler's resource remarks."""
+    use, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name is not None:
+            use[name] = int(m.group(1))
+    return use
 
 
 def build(verbose: bool = True) -> str:
@@ -64,19 +87,26 @@ def build(verbose: bool = True) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(objdir, src + ".o")
-            cmd = [hipcc(), *_common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc(), *_common_flags(RESOURCE_FLAGS), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             return obj, subprocess.run(cmd, capture_output=True, text=True)
 
         with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
             results = list(pool.map(compile_one, SOURCES))
+        spilled = []
         for (obj, res), src in zip(results, SOURCES):
             if res.returncode != 0:
                 sys.stderr.write(res.stdout + res.stderr)
                 raise RuntimeError(f"hipcc failed on {src} with exit code {res.returncode}")
-            if verbose and res.stderr.strip():
+            if verbose and _filter_stderr(res.stderr).strip():
                 sys.stderr.write(_filter_stderr(res.stderr))
+            use = scratch_use(res.stderr)
+            if src.endswith(".hip") and not use:
+                raise RuntimeError(f"no kernel resource remarks from {src}; cannot check scratch")
+            spilled += [f"{src}: {k} ({v} bytes/lane)" for k, v in use.items() if v > 0]
+        if spilled:
+            raise RuntimeError("kernels spill to scratch memory:\n  " + "\n  ".join(spilled))
         tmp = LIB_PATH + ".tmp"
         cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
                *[obj for obj, _ in results], "-o", tmp]
