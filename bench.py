@@ -259,7 +259,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--repeats", type=int, default=0,
                     help="timed windows of --steps steps each (0 = max(5, ceil(100/steps)))")
-    ap.add_argument("--config", type=int, default=0, choices=[0, 1, 2, 3, 4, 5, 6, 7, 8, 9],
+    ap.add_argument("--config", type=int, default=0, choices=list(range(12)),
                     help="workload preset (0 = the op's default: 3 for attn, 2 for append "
                          "and step, 8 for prefill)")
     ap.add_argument("--workgroups", type=int, default=0,

@@ -4,14 +4,17 @@ This module only draws inputs and lays them out in pages; it holds none of
 the attention arithmetic. Both the oracle tests and the GPU path take their
 inputs from here, so the two sides always see identical arrays.
 
-The five presets stand in for the workloads the pages talk about: a
+The five first presets stand in for the workloads the pages talk about: a
 Llama-2-7B-shaped MHA batch and a Llama-3-8B-shaped GQA batch (xLLM README,
 benchmark section; swiftLLM README, performance section), one very long
 context (the long-context case of the C++/CUDA engine blog, section 3.4), and
 a per-row INT8 cache (xLLM README, quantisation list). Two more carry the other
 storage formats the pages name: a BF16 cache (xLLM README, quantisation list:
 "FP16, BF16") on the Llama-2-7B batch, and an FP8 E4M3 cache with per-row
-scales (C++/CUDA engine blog, section 4) on the INT8 batch's shape. No weights,
+scales (C++/CUDA engine blog, section 4) on the INT8 batch's shape. Three more take the
+grouped-query shapes to the other group sizes and formats: 64 query heads over 8 KV heads
+(G = 8, the Llama-3-70B head shape) in fp16 and per-row INT8, and the Llama-3-8B batch
+(G = 4) over per-row INT8. No weights,
 prompts or datasets are involved: values are random with the stated
 distributions.
 
@@ -86,6 +89,9 @@ CONFIGS = {
     6: Config(6, "llama2_7b_mha_b48_bf16", 48, 32, 32, 128, 16, 18, 563, "bf16"),
     7: Config(7, "fp8_mha_b200", 200, 32, 32, 128, 16, 18, 530, "fp8"),
     8: Config(8, "llama3_8b_gqa_prefill_c512", 8, 32, 8, 128, 16, 512, 4096, "fp16", chunk=512),
+    9: Config(9, "llama3_70b_gqa8_b64", 64, 64, 8, 128, 16, 64, 4096, "fp16"),
+    10: Config(10, "llama3_70b_gqa8_b64_int8", 64, 64, 8, 128, 16, 64, 4096, "int8"),
+    11: Config(11, "llama3_8b_gqa_b160_int8", 160, 32, 8, 128, 16, 64, 4096, "int8"),
 }
 
 # Storage bytes per element and per row scale, by kv_dtype.
