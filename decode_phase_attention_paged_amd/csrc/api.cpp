@@ -30,7 +30,9 @@ constexpr int kSplitWorkgroupsPerCu = 1;
 // Segment mode (no merge) is the library's choice when caches are at most this many pages
 // (whole segments are then short enough to balance without cutting them) ...
 constexpr int kShortCachePages = 64;
-// ... or when every workgroup gets at least this many segments, longest first ...
+// ... or when there are at least this many segments per compute unit: over long caches the
+// grid then shrinks (down to one workgroup per compute unit) so that every workgroup gets
+// this many segments, longest first, which balances them ...
 constexpr long long kMinSegmentsPerWorkgroup = 2;
 // ... or when there are few segments but none longer than this many pages.
 constexpr int kTinyCachePages = 16;
@@ -68,18 +70,23 @@ dattn::Plan split_plan(int batch, int max_blocks, int n_kv_heads, int splits) {
 }
 
 // Segment mode on `workgroups` persistent workgroups, or (0) as many as stay resident on
-// `cus` compute units, but no more than there are segments.
+// `cus` compute units, but no more than there are segments, and over long caches no more
+// than one per kMinSegmentsPerWorkgroup segments unless that is below one per compute unit.
 dattn::Plan segment_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType kv, int group,
                          int workgroups, int cus) {
   dattn::Plan p{};
   p.mode = dattn::Mode::kSegment;
   p.num_splits = 1;
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
-  (void)max_blocks;
   if (workgroups > 0) {
     p.num_workgroups = workgroups;
   } else {
     long long wgs = static_cast<long long>(dattn::seg_workgroups_per_cu(kv, group)) * cus;
+    if (max_blocks > kShortCachePages) {
+      const long long balanced = segments / kMinSegmentsPerWorkgroup;
+      const long long cap = balanced > cus ? balanced : cus;
+      if (wgs > cap) wgs = cap;
+    }
     if (wgs > segments) wgs = segments;
     p.num_workgroups = wgs < 1 ? 1 : static_cast<int>(wgs);
   }
@@ -105,20 +112,14 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType k
     return p;
   }
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
-  // The segment-mode builds for the 1-byte formats with G = 8 keep too many registers live
-  // and spill, so the library's own plan only sends them there when the stream cannot take
-  // the batch.
-  const bool seg_spills = dattn::kv_elem_bytes(kv) == 1 && group == 8;
-  const bool seg_ok = !seg_spills || batch > dattn::kMaxBatch;
   // Segment mode needs a few segments per workgroup to balance whole segments, unless the
   // caches are short.
-  const long long seg_wgs = static_cast<long long>(dattn::seg_workgroups_per_cu(kv, group)) * cus;
-  const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * seg_wgs;
-  if (segments >= cus && seg_ok && (seg_balances || batch > dattn::kMaxBatch))
+  const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * cus;
+  if (segments >= cus && (seg_balances || batch > dattn::kMaxBatch))
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   // Few segments over caches of at most kTinyCachePages: each workgroup's run is a few
   // round trips long, so partitions would only add the merge kernel.
-  if (segments < cus && max_blocks <= kTinyCachePages && seg_ok)
+  if (segments < cus && max_blocks <= kTinyCachePages)
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   if (segments < cus) {
     const long long want = static_cast<long long>(kSplitWorkgroupsPerCu) * cus;

@@ -34,13 +34,21 @@ enum class Mode { kStream = 0, kSplit = 1, kSegment = 2 };
 
 constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
-// Waves per SIMD the segment-mode kernel is compiled for, by element width (2-byte and
-// 1-byte formats) and log2 G; the host sizes that mode's grid to the workgroups that stay
-// resident at that occupancy.
-constexpr int kSegWavesF16[4] = {1, 2, 1, 1};
-constexpr int kSegWavesI8[4] = {3, 2, 1, 1};
+// Builds whose tile products run on the matrix cores: G >= 4 over fp16, INT8 and FP8. Their
+// work per tile does not depend on G, so their tuning is one entry per element width
+// (index 0: 2-byte, 1: 1-byte); the vector-ALU builds are tuned per width and log2 G.
+constexpr bool use_mfma(KvType kv, int group) { return group >= 4 && kv != KvType::kBF16; }
+constexpr int width_index(KvType kv) { return kv_elem_bytes(kv) == 2 ? 0 : 1; }
+
+// Waves per SIMD the segment-mode kernel is compiled for; the host sizes that mode's grid
+// to the workgroups that stay resident at that occupancy.
+constexpr int kSegWavesF16[4] = {1, 2, 1, 1};   // fp16 G <= 2, bf16
+constexpr int kSegWavesI8[2] = {3, 2};          // INT8 and FP8, G <= 2
+constexpr int kSegWavesMf[2] = {1, 2};
 constexpr int seg_waves(KvType kv, int group) {
-  return kv_elem_bytes(kv) == 2 ? kSegWavesF16[log2_group(group)] : kSegWavesI8[log2_group(group)];
+  return use_mfma(kv, group)       ? kSegWavesMf[width_index(kv)]
+         : kv_elem_bytes(kv) == 2 ? kSegWavesF16[log2_group(group)]
+                                  : kSegWavesI8[log2_group(group)];
 }
 // Wavefronts of a segment-mode workgroup, which interleave the pages of its segment.
 constexpr int kSegW = 4;

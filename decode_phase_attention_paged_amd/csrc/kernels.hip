@@ -49,20 +49,24 @@ constexpr int kQLdsBytes = 16384;   // query rows a stream workgroup stages in L
 constexpr int kSplitTable = 1024;   // table entries a split workgroup stages in LDS at a time
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------------
-// Lane geometry. A lane owns one 16-byte chunk of one token row per load instruction.
-// fp16: a row is 256 B = 16 lanes; load i of a tile covers tokens 4i .. 4i+3, i.e. the
-//       contiguous bytes [1024 i, 1024 i + 1024), lane l at byte 16 l.
-// int8: a row is 128 B = 8 lanes; lane row r covers tokens 2r and 2r + 1 (loads 0 and 1)
-//       so that its two row scales are one 8-byte load.
-// bf16 takes the fp16 geometry and fp8 the int8 one.
-template <KvType kKv>
+// Lane geometry. A lane owns one chunk of one token row per load instruction.
+// fp16: a row is 256 B = 16 lanes of 16 B; load i of a tile covers tokens 4i .. 4i+3, i.e.
+//       the contiguous bytes [1024 i, 1024 i + 1024), lane l at byte 16 l.
+// int8: a row is 128 B = 8 lanes of 16 B; lane row r covers tokens 2r and 2r + 1 (loads 0
+//       and 1) so that its two row scales are one 8-byte load.
+// bf16 takes the fp16 geometry and fp8 the int8 one. These are the vector-ALU builds; G >= 4
+// over fp16, INT8 and FP8 runs on the matrix cores with its own layout (below).
+template <KvType kKv, int kGroup>
 struct Geo {
   static constexpr int kElem = kv_elem_bytes(kKv);
-  static constexpr int kChunk = 16 / kElem;                 // elements per lane per load
+  static constexpr int kLoadBytes = 16;                     // bytes per lane per load
+  static constexpr int kWords = kLoadBytes / 4;
+  static constexpr int kChunk = kLoadBytes / kElem;         // elements per lane per load
   static constexpr int kLanesPerRow = kHeadDim / kChunk;    // 16 | 8
   static constexpr int kRows = kWave / kLanesPerRow;        // lane rows: 4 | 8
   static constexpr int kLoads = kBlockSize / kRows;         // loads per tile: 4 | 2
@@ -70,57 +74,59 @@ struct Geo {
   static constexpr int kTileBytes = kBlockSize * kRowBytes;
   static constexpr bool kScaled = kv_scaled(kKv);
   static constexpr int kPairs = kChunk / 2;                 // element pairs per lane per load
+  using Load = u32x4;
 
-  __device__ static int offset(int lane, int i) {
-    if constexpr (kElem == 2) return i * 1024 + lane * 16;
-    else return (lane / kLanesPerRow) * 256 + i * 128 + (lane % kLanesPerRow) * 16;
-  }
   __device__ static int token(int row, int i) {
     if constexpr (kElem == 2) return i * kRows + row;
-    else return 2 * row + i;
+    else return kLoads * row + i;
+  }
+  __device__ static int offset(int lane, int i) {
+    if constexpr (kElem == 2) return i * 1024 + lane * 16;
+    else return token(lane / kLanesPerRow, i) * kRowBytes + (lane % kLanesPerRow) * kLoadBytes;
   }
 };
 
-// Tuning per kernel, storage type and group size (index log2 G): units kept in flight per
-// wave, and the waves per SIMD the kernel is compiled for (which caps its VGPRs at 512 /
-// waves). A larger group holds more accumulators, so it keeps fewer tiles.
+// Tuning per kernel: units kept in flight per wave, and the waves per SIMD the kernel is
+// compiled for (which caps its VGPRs at 512 / waves). Vector-ALU builds are indexed by
+// log2 G (a larger group holds more accumulators, so it keeps fewer tiles); the 1-byte
+// tables stop at G = 2 because G >= 4 over 1-byte formats runs on the matrix cores, whose
+// tables are indexed by element width (0: 2-byte, 1: 1-byte).
 constexpr int kStreamDepthF16[4] = {4, 4, 3, 2};
-constexpr int kStreamDepthI8[4] = {6, 4, 3, 2};
+constexpr int kStreamDepthI8[2] = {6, 4};
+constexpr int kStreamDepthMf[2] = {3, 3};
 constexpr int kStreamWavesF16[4] = {2, 2, 2, 1};
-constexpr int kStreamWavesI8[4] = {2, 2, 1, 1};
+constexpr int kStreamWavesI8[2] = {2, 2};
+constexpr int kStreamWavesMf[2] = {2, 1};
 // Split mode runs a few long partitions per sequence, about one workgroup per CU, so each
 // wave keeps many tiles in flight.
 constexpr int kSplitDepthF16[4] = {4, 4, 3, 2};
-// 1-byte formats with G = 8: one unit in flight; at two the build spilled about 660 bytes
-// per lane to scratch and ran three times slower.
-constexpr int kSplitDepthI8[4] = {6, 4, 3, 1};
+constexpr int kSplitDepthI8[2] = {6, 4};
+constexpr int kSplitDepthMf[2] = {3, 3};
 constexpr int kSplitWavesF16[4] = {1, 1, 1, 1};
-constexpr int kSplitWavesI8[4] = {1, 1, 1, 1};
+constexpr int kSplitWavesI8[2] = {1, 1};
+constexpr int kSplitWavesMf[2] = {1, 1};
 // Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
 // Many resident workgroups with shallow rings measured faster than deep rings.
 constexpr int kSegDepthF16[4] = {2, 2, 2, 2};
-constexpr int kSegDepthI8[4] = {1, 3, 2, 1};
+constexpr int kSegDepthI8[2] = {1, 3};
+constexpr int kSegDepthMf[2] = {2, 2};
 
 template <KvType kKv, int kGroup>
-constexpr int stream_depth() {
-  return kv_elem_bytes(kKv) == 2 ? kStreamDepthF16[log2_group(kGroup)] : kStreamDepthI8[log2_group(kGroup)];
+constexpr int pick(const int (&f16)[4], const int (&i8)[2], const int (&mf)[2]) {
+  return use_mfma(kKv, kGroup)       ? mf[width_index(kKv)]
+         : kv_elem_bytes(kKv) == 2 ? f16[log2_group(kGroup)]
+                                   : i8[log2_group(kGroup)];
 }
 template <KvType kKv, int kGroup>
-constexpr int stream_waves() {
-  return kv_elem_bytes(kKv) == 2 ? kStreamWavesF16[log2_group(kGroup)] : kStreamWavesI8[log2_group(kGroup)];
-}
+constexpr int stream_depth() { return pick<kKv, kGroup>(kStreamDepthF16, kStreamDepthI8, kStreamDepthMf); }
 template <KvType kKv, int kGroup>
-constexpr int split_depth() {
-  return kv_elem_bytes(kKv) == 2 ? kSplitDepthF16[log2_group(kGroup)] : kSplitDepthI8[log2_group(kGroup)];
-}
+constexpr int stream_waves() { return pick<kKv, kGroup>(kStreamWavesF16, kStreamWavesI8, kStreamWavesMf); }
 template <KvType kKv, int kGroup>
-constexpr int split_waves() {
-  return kv_elem_bytes(kKv) == 2 ? kSplitWavesF16[log2_group(kGroup)] : kSplitWavesI8[log2_group(kGroup)];
-}
+constexpr int split_depth() { return pick<kKv, kGroup>(kSplitDepthF16, kSplitDepthI8, kSplitDepthMf); }
 template <KvType kKv, int kGroup>
-constexpr int seg_depth() {
-  return kv_elem_bytes(kKv) == 2 ? kSegDepthF16[log2_group(kGroup)] : kSegDepthI8[log2_group(kGroup)];
-}
+constexpr int split_waves() { return pick<kKv, kGroup>(kSplitWavesF16, kSplitWavesI8, kSplitWavesMf); }
+template <KvType kKv, int kGroup>
+constexpr int seg_depth() { return pick<kKv, kGroup>(kSegDepthF16, kSegDepthI8, kSegDepthMf); }
 
 // ---------------------------------------------------------------------------------------
 // Cross-lane and conversion helpers.
@@ -179,56 +185,60 @@ __device__ __forceinline__ void fp8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
 
 // A load's elements as exact fp16 pairs (fp16, int8 and fp8 storage; bf16 values are not
 // all fp16 values and take their own path).
-template <KvType kKv>
-__device__ __forceinline__ void unpack(const u32x4& raw, h2 (&x)[Geo<kKv>::kPairs]) {
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void unpack(const typename Geo<kKv, kGroup>::Load& raw,
+                                       h2 (&x)[Geo<kKv, kGroup>::kPairs]) {
   static_assert(kKv != KvType::kBF16, "bf16 is not unpacked to fp16");
+  constexpr int kWords = Geo<kKv, kGroup>::kWords;
   if constexpr (kKv == KvType::kF16) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = as_h2(raw[e]);
+    for (int e = 0; e < kWords; ++e) x[e] = as_h2(raw[e]);
   } else if constexpr (kKv == KvType::kI8) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) i8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
+    for (int e = 0; e < kWords; ++e) i8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) fp8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
+    for (int e = 0; e < kWords; ++e) fp8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
   }
 }
 
 // q . k over this lane's elements of one load, accumulated in fp32 onto d. The query pairs
 // hold the query's raw 16-bit patterns: fp16 for every format but bf16, whose q is bf16.
-template <KvType kKv>
-__device__ __forceinline__ float dot_row(const u32x4& raw, const h2 (&q)[Geo<kKv>::kPairs]) {
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ float dot_row(const typename Geo<kKv, kGroup>::Load& raw,
+                                         const h2 (&q)[Geo<kKv, kGroup>::kPairs]) {
   float d = 0.0f;
   if constexpr (kKv == KvType::kBF16) {
 #pragma unroll
-    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+    for (int e = 0; e < Geo<kKv, kGroup>::kPairs; ++e) {
       const uint32_t word = raw[e];
       d = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(word), __builtin_bit_cast(bf2, q[e]), d, false);
     }
   } else {
-    h2 kx[Geo<kKv>::kPairs];
-    unpack<kKv>(raw, kx);
+    h2 kx[Geo<kKv, kGroup>::kPairs];
+    unpack<kKv, kGroup>(raw, kx);
 #pragma unroll
-    for (int e = 0; e < Geo<kKv>::kPairs; ++e) d = __builtin_amdgcn_fdot2(kx[e], q[e], d, false);
+    for (int e = 0; e < Geo<kKv, kGroup>::kPairs; ++e) d = __builtin_amdgcn_fdot2(kx[e], q[e], d, false);
   }
   return d;
 }
 
 // acc[j] += w * v[j] over this lane's elements of one load.
-template <KvType kKv>
-__device__ __forceinline__ void axpy_row(const u32x4& raw, float w, float (&acc)[Geo<kKv>::kChunk]) {
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void axpy_row(const typename Geo<kKv, kGroup>::Load& raw, float w,
+                                         float (&acc)[Geo<kKv, kGroup>::kChunk]) {
   if constexpr (kKv == KvType::kBF16) {
 #pragma unroll
-    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+    for (int e = 0; e < Geo<kKv, kGroup>::kPairs; ++e) {
       const uint32_t word = raw[e];
       acc[2 * e] = fmaf(w, bf16_lo(word), acc[2 * e]);
       acc[2 * e + 1] = fmaf(w, bf16_hi(word), acc[2 * e + 1]);
     }
   } else {
-    h2 vx[Geo<kKv>::kPairs];
-    unpack<kKv>(raw, vx);
+    h2 vx[Geo<kKv, kGroup>::kPairs];
+    unpack<kKv, kGroup>(raw, vx);
 #pragma unroll
-    for (int e = 0; e < Geo<kKv>::kPairs; ++e) {
+    for (int e = 0; e < Geo<kKv, kGroup>::kPairs; ++e) {
       acc[2 * e] = fmaf(w, static_cast<float>(vx[e].x), acc[2 * e]);
       acc[2 * e + 1] = fmaf(w, static_cast<float>(vx[e].y), acc[2 * e + 1]);
     }
@@ -256,25 +266,21 @@ __device__ __forceinline__ int32_t scalar_load(const int32_t* base, size_t idx) 
 
 // ---------------------------------------------------------------------------------------
 // One page tile of K and V for one KV head, held in VGPRs.
-template <KvType kKv>
+template <KvType kKv, int kGroup>
 struct Tile {
-  using Gm = Geo<kKv>;
-  u32x4 k[Gm::kLoads];
-  u32x4 v[Gm::kLoads];
-  float ks[Gm::kScaled ? 2 : 1];
-  float vs[Gm::kScaled ? 2 : 1];
+  using Gm = Geo<kKv, kGroup>;
+  typename Gm::Load k[Gm::kLoads];
+  typename Gm::Load v[Gm::kLoads];
+  float ks[Gm::kScaled ? Gm::kLoads : 1];   // row scale of the token of load i
+  float vs[Gm::kScaled ? Gm::kLoads : 1];
 };
 
 // Cache tiles are read once per step, so their loads carry the non-temporal hint: a random
 // 4 KiB tile gather streams about 13 % faster from HBM with it than without (6.7-6.9 against
 // 5.9-6.0 TB/s on MI355X), and a plain streaming read 7.0-7.2 against 6.2-6.4 TB/s.
-__device__ __forceinline__ u32x4 stream_load16(const char* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ float2 stream_load8(const float* p) {
-  const auto* q = reinterpret_cast<const float __attribute__((ext_vector_type(2)))*>(p);
-  const auto v = __builtin_nontemporal_load(q);
-  return make_float2(v.x, v.y);
+template <typename T>
+__device__ __forceinline__ T stream_load(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
 // Tile index = phys * Hkv + g. A unit whose page id failed the range check reads tile 0
@@ -284,37 +290,41 @@ __device__ __forceinline__ float2 stream_load8(const float* p) {
 // instead: their addresses fall in cache lines the wave reads anyway, so rows the softmax
 // masks out cost no HBM traffic. Other values (full pages, and units that only re-read an
 // earlier tile) load the whole tile with immediate offsets.
-template <KvType kKv>
-__device__ __forceinline__ void load_tile(Tile<kKv>& t, const Args& a, uint32_t tile_index,
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void load_tile(Tile<kKv, kGroup>& t, const Args& a, uint32_t tile_index,
                                           int lane, int valid) {
-  using Gm = Geo<kKv>;
+  using Gm = Geo<kKv, kGroup>;
+  using L = typename Gm::Load;
   const size_t base = static_cast<size_t>(tile_index) * Gm::kTileBytes;
   const char* kb = static_cast<const char*>(a.k_pages) + base;
   const char* vb = static_cast<const char*>(a.v_pages) + base;
   if (valid <= 0 || valid >= kBlockSize) {
 #pragma unroll
     for (int i = 0; i < Gm::kLoads; ++i) {
-      t.k[i] = stream_load16(kb + Gm::offset(lane, i));
-      t.v[i] = stream_load16(vb + Gm::offset(lane, i));
+      t.k[i] = stream_load<L>(kb + Gm::offset(lane, i));
+      t.v[i] = stream_load<L>(vb + Gm::offset(lane, i));
     }
   } else {
     const int row = lane / Gm::kLanesPerRow;
-    const int in_row = (lane % Gm::kLanesPerRow) * 16;
+    const int in_row = (lane % Gm::kLanesPerRow) * Gm::kLoadBytes;
 #pragma unroll
     for (int i = 0; i < Gm::kLoads; ++i) {
       const int off = min(Gm::token(row, i), valid - 1) * Gm::kRowBytes + in_row;
-      t.k[i] = stream_load16(kb + off);
-      t.v[i] = stream_load16(vb + off);
+      t.k[i] = stream_load<L>(kb + off);
+      t.v[i] = stream_load<L>(vb + off);
     }
   }
   if constexpr (Gm::kScaled) {
-    const size_t srow = static_cast<size_t>(tile_index) * kBlockSize + 2 * (lane / Gm::kLanesPerRow);
-    const float2 ks = stream_load8(a.k_scale + srow);
-    const float2 vs = stream_load8(a.v_scale + srow);
-    t.ks[0] = ks.x;
-    t.ks[1] = ks.y;
-    t.vs[0] = vs.x;
-    t.vs[1] = vs.y;
+    // The lane row's tokens are consecutive, so their row scales are one load.
+    typedef float Scales __attribute__((ext_vector_type(Gm::kLoads)));
+    const size_t srow = static_cast<size_t>(tile_index) * kBlockSize + Gm::token(lane / Gm::kLanesPerRow, 0);
+    const Scales ks = stream_load<Scales>(a.k_scale + srow);
+    const Scales vs = stream_load<Scales>(a.v_scale + srow);
+#pragma unroll
+    for (int i = 0; i < Gm::kLoads; ++i) {
+      t.ks[i] = ks[i];
+      t.vs[i] = vs[i];
+    }
   }
 }
 
@@ -325,7 +335,7 @@ template <KvType kKv, int kGroup>
 struct State {
   float m[kGroup];
   float l[kGroup];
-  float acc[kGroup][Geo<kKv>::kChunk];
+  float acc[kGroup][Geo<kKv, kGroup>::kChunk];
 };
 
 template <KvType kKv, int kGroup>
@@ -335,22 +345,22 @@ __device__ __forceinline__ void reset(State<kKv, kGroup>& st) {
     st.m[h] = kNegInf;
     st.l[h] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < Geo<kKv>::kChunk; ++j) st.acc[h][j] = 0.0f;
+    for (int j = 0; j < Geo<kKv, kGroup>::kChunk; ++j) st.acc[h][j] = 0.0f;
   }
 }
 
 // Query rows of one segment: this lane's kChunk columns of each of the G heads.
 template <KvType kKv, int kGroup>
-using QRegs = h2[kGroup][Geo<kKv>::kPairs];
+using QRegs = h2[kGroup][Geo<kKv, kGroup>::kPairs];
 
 // Fold one page tile into the running state. With kMasked, tokens at or past `valid`
 // inside the page contribute nothing, whatever their K, V or scale slots hold. The tile is
 // only read: masking works on copies.
 template <KvType kKv, int kGroup, bool kMasked>
-__device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGroup>& st,
+__device__ __forceinline__ void consume_tile(const Tile<kKv, kGroup>& t, State<kKv, kGroup>& st,
                                              const QRegs<kKv, kGroup>& qh, float scale_log2,
                                              int row, int valid) {
-  using Gm = Geo<kKv>;
+  using Gm = Geo<kKv, kGroup>;
   bool ok[Gm::kLoads];
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) ok[i] = !kMasked || Gm::token(row, i) < valid;
@@ -361,7 +371,7 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGro
     if constexpr (Gm::kScaled) f *= t.ks[i];
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      const float d = dot_row<kKv>(t.k[i], qh[h]);
+      const float d = dot_row<kKv, kGroup>(t.k[i], qh[h]);
       const float sc = row_sum<Gm::kLanesPerRow>(d) * f;
       s[h][i] = ok[i] ? sc : kNegInf;
     }
@@ -388,21 +398,21 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv>& t, State<kKv, kGro
   }
 #pragma unroll
   for (int i = 0; i < Gm::kLoads; ++i) {
-    u32x4 raw = t.v[i];
-    if constexpr (kMasked) raw = ok[i] ? raw : u32x4{0u, 0u, 0u, 0u};
+    typename Gm::Load raw = t.v[i];
+    if constexpr (kMasked) raw = ok[i] ? raw : typename Gm::Load(0u);
     float vscale = 1.0f;
     if constexpr (Gm::kScaled) vscale = ok[i] ? t.vs[i] : 0.0f;
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       float pw = p[h][i];
       if constexpr (Gm::kScaled) pw *= vscale;
-      axpy_row<kKv>(raw, pw, st.acc[h]);
+      axpy_row<kKv, kGroup>(raw, pw, st.acc[h]);
     }
   }
 }
 
 template <KvType kKv, int kGroup>
-__device__ __forceinline__ void consume(const Tile<kKv>& t, State<kKv, kGroup>& st,
+__device__ __forceinline__ void consume(const Tile<kKv, kGroup>& t, State<kKv, kGroup>& st,
                                         const QRegs<kKv, kGroup>& qh, float scale_log2, int row,
                                         int valid) {
   if (valid == kBlockSize) consume_tile<kKv, kGroup, false>(t, st, qh, scale_log2, row, kBlockSize);
@@ -422,7 +432,7 @@ __device__ __forceinline__ void merge_lanes(State<kKv, kGroup>& st, int off) {
     const float wb = fast_exp2(mo - base);
     st.l[h] = st.l[h] * wa + lo * wb;
 #pragma unroll
-    for (int j = 0; j < Geo<kKv>::kChunk; ++j) {
+    for (int j = 0; j < Geo<kKv, kGroup>::kChunk; ++j) {
       const float ao = __shfl_xor(st.acc[h][j], off);
       st.acc[h][j] = st.acc[h][j] * wa + ao * wb;
     }
@@ -435,7 +445,253 @@ __device__ __forceinline__ void merge_lanes(State<kKv, kGroup>& st, int off) {
 template <KvType kKv, int kGroup>
 __device__ __forceinline__ void merge_rows(State<kKv, kGroup>& st) {
 #pragma unroll
-  for (int off = Geo<kKv>::kLanesPerRow; off < kWave; off <<= 1) merge_lanes<kKv, kGroup>(st, off);
+  for (int off = Geo<kKv, kGroup>::kLanesPerRow; off < kWave; off <<= 1) merge_lanes<kKv, kGroup>(st, off);
+}
+
+// ---------------------------------------------------------------------------------------
+// Matrix-core tile consume, for G >= 4 over fp16, INT8 and FP8 caches. With G query heads
+// per KV head the vector-ALU consume grows with G (every head repeats the dot products, the
+// softmax and the weighted sum), and at G = 4 it kept the SIMDs 59 % busy with one wave
+// each (rocprofv3 VALU counters). Here both products of a tile run on the matrix cores,
+// with the G heads as the N columns of a 16x16 tile (columns G .. 15 hold zero queries):
+//   S^T[token][head]  = K[token][:] . Q[head][:]     v_mfma_f32_16x16x32_f16, 4 steps of 32 d
+//   O^T[d][head]     += V^T[d][token] P^T[token][head]   v_mfma_f32_16x16x16f16, 8 blocks of d
+// Operand layouts (lane l, q = l / 16): the 16x16x32 A operand holds A[l % 16][slot 8q + e],
+// B holds B[slot 8q + e][l % 16], and D holds D[4q + e][l % 16]; the 16x16x16 ones hold
+// 4 k slots per lane, A[l % 16][4q + e] and B[4q + e][l % 16]. A contraction is correct for
+// any assignment of the k values to slots that A and B share, and an output row may stand
+// for any d as long as the writer knows which:
+//  * scores: lane (q, t) holds 32 d of K[token t] and step s takes d = k_dim(q, s) + e for
+//    slot 8q + e; the query operand uses the same map. For fp16 the lane's four 16-byte
+//    loads sit at row bytes 64s + 16q, so that the four lanes of a row read one contiguous
+//    64-byte run per load instruction (16 rows x 64 bytes, the fewest cache lines a load
+//    can touch when lane l % 16 is the token); a 1-byte row is 128 bytes and the lane reads
+//    its 32-byte quarter q;
+//  * the score output leaves lane (q, n) with tokens 4q .. 4q + 3 of head n, which is the
+//    B operand (P^T) of the weighted sum as it stands, so the softmax weights never move;
+//  * weighted sum: lane (q, m) loads V[token 4q + j][d in [8m, 8m + 8)] for j < 4 (whole
+//    rows per load instruction), so output row m of block b stands for d = 8m + b, and the
+//    A operand of block b is element b of the four loaded rows, gathered with byte permutes.
+//    Lane (q, n) then ends with O[head n][d] for d = 32q + 8e + b: a contiguous 32-float run.
+// The softmax runs per head column: the tile max over 16 tokens is two cross-lane steps,
+// and the running max moves only when a tile exceeds it by more than kLazyRescale (log2
+// units), so most tiles skip the rescale and the weights, rounded to fp16 for the matrix
+// cores, stay below 2^8. INT8 and FP8 codes are widened exactly to fp16 (as in the vector
+// path); a row's K scale multiplies its score and its V scale its weight. BF16 caches keep
+// the vector path (bf16 weights would lose precision, see the chunked-prefill kernel).
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLazyRescale = 8.0f;
+
+template <KvType kKv>
+struct MGeo {
+  static constexpr int kElem = kv_elem_bytes(kKv);
+  static constexpr int kRowBytes = kHeadDim * kElem;
+  static constexpr int kTileBytes = kBlockSize * kRowBytes;
+  static constexpr int kKLoads = 32 * kElem / 16;   // 16-byte K loads per lane: 4 | 2
+  using VLoad = typename std::conditional<kElem == 2, u32x4, u32x2>::type;
+  static constexpr bool kScaled = kv_scaled(kKv);
+  // Row byte offset of K load i of lane group q, and the first d of score step s there.
+  __device__ static constexpr int k_offset(int q, int i) { return kElem == 2 ? 64 * i + 16 * q : 32 * q + 16 * i; }
+  __device__ static constexpr int k_dim(int q, int s) { return kElem == 2 ? 32 * s + 8 * q : 32 * q + 8 * s; }
+};
+
+template <KvType kKv>
+struct MTile {
+  u32x4 k[MGeo<kKv>::kKLoads];
+  typename MGeo<kKv>::VLoad v[4];
+  f4 ks, vs;   // row scales of tokens 4q .. 4q + 3 (1-byte formats)
+};
+
+struct MState {
+  float m;     // running max of head l % 16 (log2 units), the same in its four lanes
+  float l;     // this lane's share of the running sum
+  f4 o[8];     // O[head l % 16][32q + 8e + b] in o[b][e]
+};
+
+struct MQ {
+  h8 s[4];     // Q[head l % 16][k_dim(q, s) ..  + 7] for score step s (zero past G)
+};
+
+__device__ __forceinline__ void mreset(MState& st) {
+  st.m = kNegInf;
+  st.l = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) st.o[b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// Same tile index and partial-page rule as load_tile: rows at or past `valid` re-read the
+// last valid row.
+template <KvType kKv>
+__device__ __forceinline__ void mload_tile(MTile<kKv>& t, const Args& a, uint32_t tile_index,
+                                           int lane, int valid) {
+  using Gm = MGeo<kKv>;
+  using VL = typename Gm::VLoad;
+  const size_t base = static_cast<size_t>(tile_index) * Gm::kTileBytes;
+  const char* kb = static_cast<const char*>(a.k_pages) + base;
+  const char* vb = static_cast<const char*>(a.v_pages) + base;
+  const int q = lane >> 4;
+  const int c = lane & 15;
+  const bool clamp = valid > 0 && valid < kBlockSize;
+  const int tk = clamp ? min(c, valid - 1) : c;
+  const char* krow = kb + tk * Gm::kRowBytes;
+#pragma unroll
+  for (int i = 0; i < Gm::kKLoads; ++i) t.k[i] = stream_load<u32x4>(krow + Gm::k_offset(q, i));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tv = clamp ? min(4 * q + j, valid - 1) : 4 * q + j;
+    t.v[j] = stream_load<VL>(vb + tv * Gm::kRowBytes + c * 8 * Gm::kElem);
+  }
+  if constexpr (Gm::kScaled) {
+    const size_t srow = static_cast<size_t>(tile_index) * kBlockSize + 4 * q;
+    t.ks = stream_load<f4>(a.k_scale + srow);
+    t.vs = stream_load<f4>(a.v_scale + srow);
+  }
+}
+
+// Eight K values of score step s as an fp16 operand.
+template <KvType kKv>
+__device__ __forceinline__ h8 mk_operand(const MTile<kKv>& t, int s) {
+  if constexpr (kKv == KvType::kF16) {
+    return __builtin_bit_cast(h8, t.k[s]);
+  } else {
+    const u32x4 w = t.k[s >> 1];
+    h2 x[4];
+    const uint32_t w0 = (s & 1) ? w[2] : w[0];
+    const uint32_t w1 = (s & 1) ? w[3] : w[1];
+    if constexpr (kKv == KvType::kI8) {
+      i8x4_to_h2(w0, x[0], x[1]);
+      i8x4_to_h2(w1, x[2], x[3]);
+    } else {
+      fp8x4_to_h2(w0, x[0], x[1]);
+      fp8x4_to_h2(w1, x[2], x[3]);
+    }
+    return h8{x[0].x, x[0].y, x[1].x, x[1].y, x[2].x, x[2].y, x[3].x, x[3].y};
+  }
+}
+
+// The four V rows of the lane as fp16 words (word w of row j holds d = 8m + 2w, 8m + 2w + 1).
+template <KvType kKv>
+__device__ __forceinline__ void mv_words(const MTile<kKv>& t, u32x4 (&v)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (kKv == KvType::kF16) {
+      v[j] = t.v[j];
+    } else {
+      h2 x[4];
+      if constexpr (kKv == KvType::kI8) {
+        i8x4_to_h2(t.v[j][0], x[0], x[1]);
+        i8x4_to_h2(t.v[j][1], x[2], x[3]);
+      } else {
+        fp8x4_to_h2(t.v[j][0], x[0], x[1]);
+        fp8x4_to_h2(t.v[j][1], x[2], x[3]);
+      }
+      v[j] = u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
+                   __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])};
+    }
+  }
+}
+
+template <KvType kKv, bool kMasked>
+__device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, const MQ& qm,
+                                              float scale_log2, int lane, int valid) {
+  const int q = lane >> 4;
+  f4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(mk_operand<kKv>(t, s), qm.s[s], sc, 0, 0, 0);
+  float sv[4];
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float f = scale_log2;
+    if constexpr (MGeo<kKv>::kScaled) f *= t.ks[j];
+    sv[j] = sc[j] * f;
+    if constexpr (kMasked) sv[j] = 4 * q + j < valid ? sv[j] : kNegInf;
+    mx = fmaxf(mx, sv[j]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool grow = mx > st.m + kLazyRescale;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float m_new = grow ? mx : st.m;
+    const float alpha = grow ? fast_exp2(st.m - m_new) : 1.0f;
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) st.o[b] *= alpha;
+    st.m = m_new;
+  }
+  const float base = st.m == kNegInf ? 0.0f : st.m;
+  h4 pw;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float p = fast_exp2(sv[j] - base);
+    st.l += p;
+    if constexpr (MGeo<kKv>::kScaled) {
+      const bool ok = !kMasked || 4 * q + j < valid;
+      p *= ok ? t.vs[j] : 0.0f;
+    }
+    pw[j] = static_cast<_Float16>(p);
+  }
+  u32x4 v[4];
+  mv_words<kKv>(t, v);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    // Element b of the four rows: rows 0, 1 into the first word and rows 2, 3 into the
+    // second (low halves for even b, high halves for odd b).
+    const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+    const uint32_t lo = __builtin_amdgcn_perm(v[1][b >> 1], v[0][b >> 1], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(v[3][b >> 1], v[2][b >> 1], sel);
+    const h4 va = __builtin_bit_cast(h4, u32x2{lo, hi});
+    st.o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pw, st.o[b], 0, 0, 0);
+  }
+}
+
+template <KvType kKv>
+__device__ __forceinline__ void mconsume(const MTile<kKv>& t, MState& st, const MQ& qm,
+                                         float scale_log2, int lane, int valid) {
+  if (valid == kBlockSize) mconsume_tile<kKv, false>(t, st, qm, scale_log2, lane, kBlockSize);
+  else mconsume_tile<kKv, true>(t, st, qm, scale_log2, lane, valid);
+}
+
+// The query operand from a segment's query rows, G x D fp16 laid out head-major at `rows`
+// (global memory or LDS): for step s lane (q, n) takes head n's d from k_dim(q, s), zero
+// past G.
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void mload_q(MQ& qm, const u32x4* rows, int lane) {
+  const int q = lane >> 4;
+  const int n = lane & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (n < kGroup) w = rows[(n * kHeadDim + MGeo<kKv>::k_dim(q, s)) / 8];
+    qm.s[s] = __builtin_bit_cast(h8, w);
+  }
+}
+
+// The wave's state for the merge across waves: per head n < G its running max, its sum (the
+// four lanes of column n added) and its 128 unnormalised outputs.
+template <int kGroup>
+__device__ __forceinline__ void mpublish(const MState& st, float* acc, float* m, float* l, int lane) {
+  const int q = lane >> 4;
+  const int n = lane & 15;
+  float sum = st.l;
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  if (n < kGroup) {
+    float* o = acc + n * kHeadDim + 32 * q;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<float4*>(o + 8 * e) = make_float4(st.o[0][e], st.o[1][e], st.o[2][e], st.o[3][e]);
+      *reinterpret_cast<float4*>(o + 8 * e + 4) = make_float4(st.o[4][e], st.o[5][e], st.o[6][e], st.o[7][e]);
+    }
+    if (q == 0) {
+      m[n] = st.m;
+      l[n] = sum;
+    }
+  }
 }
 
 __device__ __forceinline__ void store_chunk(float* dst, const float* src, int n) {
@@ -443,21 +699,115 @@ __device__ __forceinline__ void store_chunk(float* dst, const float* src, int n)
     *reinterpret_cast<float4*>(dst + j) = make_float4(src[j], src[j + 1], src[j + 2], src[j + 3]);
 }
 
-// Load this lane's columns of the query rows at byte offset `row_off` of q (global).
+// The tile consume a (G, format) build takes in every mode: the matrix cores
+// for G >= 4 over fp16, INT8 and FP8, the vector ALU otherwise.
 template <KvType kKv, int kGroup>
-__device__ __forceinline__ void load_query_global(QRegs<kKv, kGroup>& qh, const void* q,
-                                                  size_t row_off, int col) {
-  using Gm = Geo<kKv>;
+struct Path {
+  static constexpr bool kMf = use_mfma(kKv, kGroup);
+  using Gm = Geo<kKv, kGroup>;
+  struct QV {
+    QRegs<kKv, kGroup> v;
+  };
+  using TileT = typename std::conditional<kMf, MTile<kKv>, Tile<kKv, kGroup>>::type;
+  using StateT = typename std::conditional<kMf, MState, State<kKv, kGroup>>::type;
+  using QT = typename std::conditional<kMf, MQ, QV>::type;
+
+  __device__ __forceinline__ static void reset_state(StateT& st) {
+    if constexpr (kMf) mreset(st);
+    else reset(st);
+  }
+  __device__ __forceinline__ static void load(TileT& t, const Args& a, uint32_t tile_index,
+                                              int lane, int valid) {
+    if constexpr (kMf) mload_tile<kKv>(t, a, tile_index, lane, valid);
+    else load_tile<kKv, kGroup>(t, a, tile_index, lane, valid);
+  }
+  __device__ __forceinline__ static void consume_unit(const TileT& t, StateT& st, const QT& q,
+                                                      float scale_log2, int lane, int valid) {
+    if constexpr (kMf) mconsume<kKv>(t, st, q, scale_log2, lane, valid);
+    else consume<kKv, kGroup>(t, st, q.v, scale_log2, lane / Gm::kLanesPerRow, valid);
+  }
+  // Query operand of a segment whose G query rows (head-major, fp16 or bf16) are at `rows`.
+  __device__ __forceinline__ static void load_q(QT& q, const u32x4* rows, int lane) {
+    if constexpr (kMf) {
+      mload_q<kKv, kGroup>(q, rows, lane);
+    } else {
+      const int col = lane % Gm::kLanesPerRow;
 #pragma unroll
-  for (int h = 0; h < kGroup; ++h)
+      for (int h = 0; h < kGroup; ++h)
 #pragma unroll
-    for (int c = 0; c < Gm::kChunk / 8; ++c) {
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(
-          static_cast<const char*>(q) + row_off + h * kHeadDim * 2 + (col * Gm::kChunk + c * 8) * 2);
+        for (int c = 0; c < Gm::kChunk / 8; ++c) {
+          const u32x4 raw = rows[(h * kHeadDim * 2 + (col * Gm::kChunk + c * 8) * 2) / 16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
+          for (int e = 0; e < 4; ++e) q.v[h][c * 4 + e] = as_h2(raw[e]);
+        }
     }
-}
+  }
+  // The wave's state for the merge across waves: per head its running max (log2 units),
+  // sum and 128 unnormalised outputs, at m[h], l[h] and acc[h * 128 ..].
+  __device__ __forceinline__ static void publish(StateT& st, float* acc, float* m, float* l,
+                                                 int lane) {
+    if constexpr (kMf) {
+      mpublish<kGroup>(st, acc, m, l, lane);
+    } else {
+      merge_rows<kKv, kGroup>(st);
+      const int row = lane / Gm::kLanesPerRow;
+      const int col = lane % Gm::kLanesPerRow;
+      if (row == 0) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+          for (int j = 0; j < Gm::kChunk; ++j) acc[h * kHeadDim + col * Gm::kChunk + j] = st.acc[h][j];
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+          m[h] = st.m[h];
+          l[h] = st.l[h];
+        }
+      }
+    }
+  }
+  // The normalised result of the state: o[h * 128 + d] = acc / l and, unless lse is null,
+  // lse[h] = (m + log2 l) * lse_mul; NaN everywhere for a bad segment.
+  __device__ __forceinline__ static void store_normalised(StateT& st, float* o, float* lse,
+                                                          float lse_mul, bool bad, int lane) {
+    const float nan = __builtin_nanf("");
+    if constexpr (kMf) {
+      const int q = lane >> 4;
+      const int n = lane & 15;
+      float sum = st.l;
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      if (n < kGroup) {
+        const float inv = 1.0f / sum;
+        float* row = o + n * kHeadDim + 32 * q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float4 lo = make_float4(st.o[0][e], st.o[1][e], st.o[2][e], st.o[3][e]);
+          float4 hi = make_float4(st.o[4][e], st.o[5][e], st.o[6][e], st.o[7][e]);
+          lo = bad ? make_float4(nan, nan, nan, nan) : make_float4(lo.x * inv, lo.y * inv, lo.z * inv, lo.w * inv);
+          hi = bad ? make_float4(nan, nan, nan, nan) : make_float4(hi.x * inv, hi.y * inv, hi.z * inv, hi.w * inv);
+          *reinterpret_cast<float4*>(row + 8 * e) = lo;
+          *reinterpret_cast<float4*>(row + 8 * e + 4) = hi;
+        }
+        if (q == 0 && lse != nullptr) lse[n] = bad ? nan : (st.m + __log2f(sum)) * lse_mul;
+      }
+    } else {
+      merge_rows<kKv, kGroup>(st);
+      const int row = lane / Gm::kLanesPerRow;
+      const int col = lane % Gm::kLanesPerRow;
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        const float inv = 1.0f / st.l[h];
+        float v[Gm::kChunk];
+#pragma unroll
+        for (int j = 0; j < Gm::kChunk; ++j) v[j] = bad ? nan : st.acc[h][j] * inv;
+        if (row == 0) store_chunk(o + h * kHeadDim + col * Gm::kChunk, v, Gm::kChunk);
+        if (lane == 0 && lse != nullptr) lse[h] = bad ? nan : (st.m[h] + __log2f(st.l[h])) * lse_mul;
+      }
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------------------
 // Stream mode. Per sequence the workgroup keeps in LDS its first unit (s_pre) and its
@@ -541,33 +891,19 @@ __device__ __forceinline__ Rec make_rec(const Cursor& c, int32_t phys, const Arg
 // write the normalised output (the whole segment was here) or leave the piece in a slot
 // for the merge kernel, recording where all the pieces are if this is the first one.
 template <KvType kKv, int kGroup>
-__device__ __forceinline__ void finish_piece(const Args& a, State<kKv, kGroup>& st, uint32_t lin,
-                                             bool seg_first, bool seg_whole, bool seg_bad,
-                                             bool last_page, uint32_t seg_end, uint32_t worker,
-                                             uint32_t workers, uint32_t total_units, int row,
-                                             int col, int lane, int32_t (&record)[4]) {
-  using Gm = Geo<kKv>;
-  merge_rows<kKv, kGroup>(st);
+__device__ __forceinline__ void finish_piece(const Args& a, typename Path<kKv, kGroup>::StateT& st,
+                                             uint32_t lin, bool seg_first, bool seg_whole,
+                                             bool seg_bad, bool last_page, uint32_t seg_end,
+                                             uint32_t worker, uint32_t workers,
+                                             uint32_t total_units, int lane, int32_t (&record)[4]) {
   const bool complete = last_page && seg_whole;
   const int slot = static_cast<int>(worker) * kPieceSlots + (seg_first ? 0 : 1);
-  const float nan = __builtin_nanf("");
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    const float inv = 1.0f / st.l[h];
-    const float lse2 = seg_bad ? nan : st.m[h] + __log2f(st.l[h]);
-    float o[Gm::kChunk];
-#pragma unroll
-    for (int j = 0; j < Gm::kChunk; ++j) o[j] = seg_bad ? nan : st.acc[h][j] * inv;
-    const size_t qrow = static_cast<size_t>(lin) * kGroup + h;
-    if (complete) {
-      if (row == 0) store_chunk(a.out + qrow * kHeadDim + col * Gm::kChunk, o, Gm::kChunk);
-      if (lane == 0 && a.lse_out != nullptr) a.lse_out[qrow] = lse2 * kLn2;
-    } else {
-      const size_t prow = static_cast<size_t>(slot) * kGroup + h;
-      if (row == 0) store_chunk(a.part_o + prow * kHeadDim + col * Gm::kChunk, o, Gm::kChunk);
-      if (lane == 0) a.part_lse[prow] = lse2;
-    }
-  }
+  // A whole segment goes to the output (lse in natural-log units), a piece to its slot.
+  const size_t qrow = static_cast<size_t>(lin) * kGroup;
+  const size_t prow = static_cast<size_t>(slot) * kGroup;
+  float* o = complete ? a.out + qrow * kHeadDim : a.part_o + prow * kHeadDim;
+  float* lse = complete ? (a.lse_out != nullptr ? a.lse_out + qrow : nullptr) : a.part_lse + prow;
+  Path<kKv, kGroup>::store_normalised(st, o, lse, complete ? kLn2 : 1.0f, seg_bad, lane);
   if (!complete && seg_whole) {
     // First piece of a segment that continues into later workers; its last piece is in
     // the last worker w' with unit_begin(w') <= seg_end - 1, i.e. w' = ceil(seg_end W / T) - 1.
@@ -585,10 +921,8 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
                                            const uint32_t* s_seq, const u32x4* s_q, uint32_t q_lin0,
                                            uint32_t worker, uint32_t workers, uint32_t total_units,
                                            int lane) {
-  using Gm = Geo<kKv>;
+  using P = Path<kKv, kGroup>;
   constexpr int kQRowBytes = kGroup * kHeadDim * 2;
-  const int row = lane / Gm::kLanesPerRow;
-  const int col = lane % Gm::kLanesPerRow;
   const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
   const uint32_t u0 = unit_begin(worker, total_units, workers);
   const uint32_t n = unit_begin(worker + 1, total_units, workers) - u0;
@@ -618,51 +952,40 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
     };
 
     Rec rec[kDepth];
-    Tile<kKv> tiles[kDepth];
+    typename P::TileT tiles[kDepth];
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
       if constexpr (d == 0) rec[0] = take();
       else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+      P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
 
-    State<kKv, kGroup> st;
-    reset(st);
-    QRegs<kKv, kGroup> qh;
+    typename P::StateT st;
+    P::reset_state(st);
+    typename P::QT qh;
     uint32_t seg_lin = 0;
     bool seg_first = true;      // the segment is this worker's first
     bool seg_whole = false;     // the segment started inside this worker (at page 0)
     bool seg_bad = false;
 
-    auto process = [&](uint32_t k, const Rec& r, const Tile<kKv>& t) {
+    auto process = [&](uint32_t k, const Rec& r, const typename P::TileT& t) {
       if (k == 0 || r.j == 0) {   // a segment starts: fetch its query rows
         seg_first = k == 0;
         seg_whole = r.j == 0;
         seg_lin = r.lin;
         seg_bad = false;
-        if constexpr (kQInLds) {
-#pragma unroll
-          for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-            for (int c = 0; c < Gm::kChunk / 8; ++c) {
-              const uint32_t off = (r.lin - q_lin0) * kQRowBytes + h * kHeadDim * 2 +
-                                   (col * Gm::kChunk + c * 8) * 2;
-              const u32x4 raw = s_q[off / 16];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
-            }
-        } else {
-          load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(r.lin) * kQRowBytes, col);
-        }
+        if constexpr (kQInLds)
+          P::load_q(qh, s_q + (r.lin - q_lin0) * (kQRowBytes / 16), lane);
+        else
+          P::load_q(qh, static_cast<const u32x4*>(a.q) + static_cast<size_t>(r.lin) * (kQRowBytes / 16), lane);
       }
       seg_bad |= !r.ok;
-      consume<kKv, kGroup>(t, st, qh, a.scale_log2, row, r.valid);
+      P::consume_unit(t, st, qh, a.scale_log2, lane, r.valid);
       const bool last_page = r.j + 1 == r.nb;
       if (last_page || k + 1 == n) {
         finish_piece<kKv, kGroup>(a, st, seg_lin, seg_first, seg_whole, seg_bad, last_page,
-                                  u0 + k - r.j + r.nb, worker, workers, total_units, row, col,
-                                  lane, record);
-        reset(st);
+                                  u0 + k - r.j + r.nb, worker, workers, total_units, lane, record);
+        P::reset_state(st);
       }
     };
 
@@ -676,7 +999,7 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
         const uint32_t k = k0 + d;
         process(k, rec[d], tiles[d]);
         if (k + kDepth < n) rec[d] = take();
-        load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+        P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
     static_for<0, kDepth>([&](auto dc) {
@@ -921,7 +1244,7 @@ template <KvType kKv, int kGroup>
 __global__ __launch_bounds__(kSegThreads)
 __attribute__((amdgpu_waves_per_eu(seg_waves(kKv, kGroup), seg_waves(kKv, kGroup))))
 void seg_kernel(Args a) {
-  using Gm = Geo<kKv>;
+  using P = Path<kKv, kGroup>;
   constexpr int kDepth = seg_depth<kKv, kGroup>();
   constexpr uint32_t kQRow16 = kGroup * kHeadDim * 2 / 16;   // 16-byte words per segment's queries
   constexpr uint32_t kChunk = kSegQBytes / (kQRow16 * 16);  // segments per staged chunk
@@ -937,8 +1260,6 @@ void seg_kernel(Args a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int row = lane / Gm::kLanesPerRow;
-  const int col = lane % Gm::kLanesPerRow;
   const int batch = a.batch;
   const uint32_t hkv = static_cast<uint32_t>(a.n_kv_heads);
   const uint32_t mb = static_cast<uint32_t>(a.max_blocks);
@@ -1022,17 +1343,9 @@ void seg_kernel(Args a) {
     stage_store(k0);
   };
 
-  QRegs<kKv, kGroup> qh;
+  typename P::QT qh;
   auto load_q = [&](uint32_t k) __attribute__((always_inline)) {
-    const uint32_t base = (k % kChunk) * kQRow16 * 16;
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-      for (int c = 0; c < Gm::kChunk / 8; ++c) {
-        const u32x4 raw = s_q[(base + h * kHeadDim * 2 + (col * Gm::kChunk + c * 8) * 2) / 16];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qh[h][c * 4 + e] = as_h2(raw[e]);
-      }
+    P::load_q(qh, s_q + (k % kChunk) * kQRow16, lane);
   };
 
   // 3. This wave's cursor: segment k, page j (j = wave, wave + 4, ...), skipping segments
@@ -1061,7 +1374,7 @@ void seg_kernel(Args a) {
     L.head_of<true>(0, b0, g0);
     const int32_t first_page =
         static_cast<uint32_t>(wave) < mb ? scalar_load(a.block_table, static_cast<size_t>(b0) * mb + wave) : 0;
-    load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(b0 * hkv + g0) * kQRow16 * 16, col);
+    P::load_q(qh, q16 + static_cast<size_t>(b0 * hkv + g0) * kQRow16, lane);
     seek();
     if (ck < L.n)
       phys_next = ck == 0 ? first_page : scalar_load(a.block_table, static_cast<size_t>(cb) * mb + cj);
@@ -1093,19 +1406,19 @@ void seg_kernel(Args a) {
   };
 
   SegRec rec[kDepth];
-  Tile<kKv> tiles[kDepth];
+  typename P::TileT tiles[kDepth];
   static_for<0, kDepth>([&](auto dc) {
     constexpr int d = decltype(dc)::value;
     rec[d] = take();
-    load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+    P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
   });
   // The first chunk of query rows goes to LDS only now, behind the first tile loads: the
   // first segment's rows are already on their way to registers.
   stage_load(0);
   stage_store(0);   // read only after the barrier of the first segment's end
 
-  State<kKv, kGroup> st;
-  reset(st);
+  typename P::StateT st;
+  P::reset_state(st);
   bool seg_bad = false;
   uint32_t cur = 0;   // segment whose state st holds
 
@@ -1114,22 +1427,9 @@ void seg_kernel(Args a) {
   // starts one. Every wave calls this exactly once per segment, in order, so the barriers
   // pair up.
   auto finish = [&](uint32_t k) __attribute__((always_inline)) {
-    merge_rows<kKv, kGroup>(st);
     const uint32_t slot = k & 1u;
-    if (row == 0) {
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-        for (int j = 0; j < Gm::kChunk; ++j) sm_acc[slot][wave][h][col * Gm::kChunk + j] = st.acc[h][j];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) {
-        sm_m[slot][wave][h] = st.m[h];
-        sm_l[slot][wave][h] = st.l[h];
-      }
-      sm_bad[slot][wave] = seg_bad ? 1 : 0;
-    }
+    P::publish(st, &sm_acc[slot][wave][0][0], &sm_m[slot][wave][0], &sm_l[slot][wave][0], lane);
+    if (lane == 0) sm_bad[slot][wave] = seg_bad ? 1 : 0;
     __syncthreads();
     const SegInfo s = L.info(k);
     bool any_bad = s.bad;
@@ -1164,7 +1464,7 @@ void seg_kernel(Args a) {
   auto next_segment = [&]() __attribute__((always_inline)) {
     finish(cur);
     ++cur;
-    reset(st);
+    P::reset_state(st);
     seg_bad = false;
     if (cur < L.n) load_q(cur);
   };
@@ -1177,10 +1477,10 @@ void seg_kernel(Args a) {
       if (rec[d].live) {
         while (cur < rec[d].k) next_segment();
         seg_bad |= !rec[d].ok;
-        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+        P::consume_unit(tiles[d], st, qh, a.scale_log2, lane, rec[d].valid);
       }
       rec[d] = take();
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+      P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
   }
   while (cur < L.n) next_segment();
@@ -1194,7 +1494,7 @@ template <KvType kKv, int kGroup>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(split_waves<kKv, kGroup>(), split_waves<kKv, kGroup>())))
 void split_kernel(Args a) {
-  using Gm = Geo<kKv>;
+  using P = Path<kKv, kGroup>;
   constexpr int kDepth = split_depth<kKv, kGroup>();
   __shared__ float sm_acc[kWaves][kGroup][kHeadDim];
   __shared__ float sm_m[kWaves][kGroup];
@@ -1204,8 +1504,6 @@ void split_kernel(Args a) {
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int row = lane / Gm::kLanesPerRow;
-  const int col = lane % Gm::kLanesPerRow;
 
   int wg = blockIdx.x;
   const int split = wg % a.num_splits;
@@ -1223,11 +1521,11 @@ void split_kernel(Args a) {
   if (j0 >= j1) return;
 
   const uint32_t lin = static_cast<uint32_t>(b) * hkv + g;
-  QRegs<kKv, kGroup> qh;
-  load_query_global<kKv, kGroup>(qh, a.q, static_cast<size_t>(lin) * kGroup * kHeadDim * 2, col);
+  typename P::QT qh;
+  P::load_q(qh, static_cast<const u32x4*>(a.q) + static_cast<size_t>(lin) * kGroup * kHeadDim * 2 / 16, lane);
 
-  State<kKv, kGroup> st;
-  reset(st);
+  typename P::StateT st;
+  P::reset_state(st);
   bool bad = bad_len;
   // The partition's table entries go through LDS, kSplitTable pages at a time, so the
   // streaming loop reads page ids with short LDS loads instead of scalar global loads.
@@ -1253,47 +1551,33 @@ void split_kernel(Args a) {
       return r;
     };
     Rec rec[kDepth];
-    Tile<kKv> tiles[kDepth];
+    typename P::TileT tiles[kDepth];
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
       if constexpr (d == 0) rec[0] = take();
       else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
-      load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+      P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
     uint32_t k0 = 0;
     for (; k0 + kDepth <= n; k0 += kDepth) {
       static_for<0, kDepth>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
         bad |= !rec[d].ok;
-        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+        P::consume_unit(tiles[d], st, qh, a.scale_log2, lane, rec[d].valid);
         if (k0 + d + kDepth < n) rec[d] = take();
-        load_tile<kKv>(tiles[d], a, rec[d].tile, lane, rec[d].valid);
+        P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
       if (k0 + d < n) {
         bad |= !rec[d].ok;
-        consume<kKv, kGroup>(tiles[d], st, qh, a.scale_log2, row, rec[d].valid);
+        P::consume_unit(tiles[d], st, qh, a.scale_log2, lane, rec[d].valid);
       }
     });
   }
-  merge_rows<kKv, kGroup>(st);
-
-  if (row == 0) {
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h)
-#pragma unroll
-      for (int j = 0; j < Gm::kChunk; ++j) sm_acc[wave][h][col * Gm::kChunk + j] = st.acc[h][j];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      sm_m[wave][h] = st.m[h];
-      sm_l[wave][h] = st.l[h];
-    }
-    sm_bad[wave] = bad ? 1 : 0;
-  }
+  P::publish(st, &sm_acc[wave][0][0], &sm_m[wave][0], &sm_l[wave][0], lane);
+  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
 
   bool any_bad = false;

@@ -196,7 +196,7 @@ def test_split_requests_round_to_whole_partitions(lib, binding):
 
 
 def test_auto_plan_for_the_preset_shapes(lib, binding):
-    # (batch, MB, Hq, Hkv) of the five preset workloads on a 256-CU device.
+    # (batch, MB, Hq, Hkv) of the preset workloads on a 256-CU device.
     p1 = plan(lib, binding, 1, 16, 8, 8)
     p2 = plan(lib, binding, 48, 36, 32, 32)
     p3 = plan(lib, binding, 160, 256, 32, 8)
@@ -208,19 +208,27 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     assert (p2.mode, p2.num_splits, p2.num_workgroups) == (binding.MODE_SEGMENT, 1, 256)
     assert (p5.mode, p5.num_splits, p5.num_workgroups) == (binding.MODE_SEGMENT, 1, 768)
     assert p2.workspace_bytes == 0 and p5.workspace_bytes == 0
-    # Never more workgroups than segments; the INT8 build for G = 8 spills, so it stays in
-    # stream mode.
+    # Never more workgroups than segments; every format takes segment mode for many short
+    # caches, G = 8 included.
     assert plan(lib, binding, 3, 8, 1, 1, cus=4).num_workgroups == 3
     assert plan(lib, binding, 3, 8, 8, 8, cus=30).num_workgroups == 24
     assert plan(lib, binding, 3, 8, 8, 8, cus=20).num_workgroups == 20
     assert plan(lib, binding, 300, 8, 8, 1, cus=2).mode == binding.MODE_SEGMENT
-    assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=1).mode == binding.MODE_STREAM
+    assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=1).mode == binding.MODE_SEGMENT
+    assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=3).mode == binding.MODE_SEGMENT
     assert plan(lib, binding, 300, 8, 8, 4, cus=2).mode == binding.MODE_SEGMENT
     # Many pairs over long caches: segment mode while every workgroup gets two segments or
     # more (1280 pairs, 256 workgroups for G = 4), else the balanced stream.
     assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 256
     s3 = plan(lib, binding, 60, 256, 32, 8)
     assert s3.mode == binding.MODE_STREAM and s3.num_workgroups == 512
+    # 64 x 8 pairs of G = 8 over 256-page INT8 caches (two pairs per CU): segment mode, with
+    # the grid cut from the two workgroups per CU the build keeps resident to one, so that
+    # each workgroup still gets two segments; 160 x 8 INT8 pairs keep both.
+    p10 = plan(lib, binding, 64, 256, 64, 8, kv=1)
+    assert (p10.mode, p10.num_workgroups) == (binding.MODE_SEGMENT, 256)
+    p11 = plan(lib, binding, 160, 256, 32, 8, kv=1)
+    assert (p11.mode, p11.num_workgroups) == (binding.MODE_SEGMENT, 512)
     # Few long caches: split mode, about one workgroup per CU.
     assert (p4.mode, p4.num_splits, p4.pages_per_split, p4.num_workgroups) == (
         binding.MODE_SPLIT, 32, 256, 256)

@@ -305,13 +305,21 @@ def test_page_permutation_is_bitwise_invariant(torch, lib, plan):
 
 
 def test_gqa_matches_repeated_mha(torch, lib):
+    """G = 4 against the same heads as MHA (K/V repeated per query head). The G = 4 build
+    runs on the matrix cores, which take each softmax weight rounded to fp16 (relative error
+    at most 2^-11; the normaliser sums the unrounded weights), while G = 1 keeps fp32
+    weights: the outputs may differ by at most 2^-11 max|V| per row, plus fp16 underflow of
+    weights below 2^-14 (at most 2^-25 each, L <= 300 of them here)."""
     w = generate(SMALL, seed=13)
-    a, _ = gpu_run(torch, lib, w, num_workgroups=1)
+    a, lse_a = gpu_run(torch, lib, w, num_workgroups=1)
     group = SMALL.n_q_heads // SMALL.n_kv_heads
     w.k_pages = np.repeat(w.k_pages, group, axis=1)
     w.v_pages = np.repeat(w.v_pages, group, axis=1)
-    b, _ = gpu_run(torch, lib, w, num_workgroups=1)
-    np.testing.assert_allclose(a, b, rtol=1e-5, atol=1e-6)
+    b, lse_b = gpu_run(torch, lib, w, num_workgroups=1)
+    vmax = float(np.abs(w.v_pages.astype(np.float64)).max())
+    bound = 2.0 ** -11 * vmax + SMALL.len_hi * 2.0 ** -25 * vmax + 1e-6
+    np.testing.assert_allclose(a, b, rtol=0, atol=bound)
+    np.testing.assert_allclose(lse_a, lse_b, rtol=1e-6, atol=1e-5)
 
 
 def test_int8_unit_scales_match_fp16_on_same_integers(torch, lib):
@@ -406,7 +414,7 @@ def test_one_hip_runtime_and_native_library(torch, lib):
 
 # ------------------------------------------------------------------ the preset workloads
 
-@pytest.mark.parametrize("index", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("index", [1, 2, 3, 4, 5, 6, 7, 9, 10, 11])
 def test_preset_workload_full_size(torch, lib, index):
     """Each preset at its full size, in the launch configuration the benchmark times
     (library-chosen grid), compared elementwise on every output."""
