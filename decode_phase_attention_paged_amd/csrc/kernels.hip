@@ -283,6 +283,13 @@ __device__ __forceinline__ T stream_load(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
+// A ring slot with no unit left keeps loading, so that every wait on the ring stays an
+// exact vmcnt count, but it loads a tile it has already read with this many valid tokens:
+// every lane then reads the tile's first row, one or two cache lines. Re-reading whole tiles
+// instead cost HBM traffic: non-temporal lines are not kept in L2 for a second read (one
+// extra tile per wave per slot, 3-4 % of the bytes of a step).
+constexpr int kIdleValid = 1;
+
 // Tile index = phys * Hkv + g. A unit whose page id failed the range check reads tile 0
 // instead (its output is NaN whatever is read), so every load targets a valid tile.
 // `valid` is the number of the page's tokens inside the sequence. On a partly filled last
@@ -955,8 +962,14 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
     typename P::TileT tiles[kDepth];
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      if constexpr (d == 0) rec[0] = take();
-      else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
+      if constexpr (d == 0) {
+        rec[0] = take();
+      } else if (static_cast<uint32_t>(d) < n) {
+        rec[d] = take();
+      } else {
+        rec[d] = rec[d - 1];
+        rec[d].valid = kIdleValid;
+      }
       P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
 
@@ -990,8 +1003,7 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
     };
 
     // Steady state: consume the oldest unit, refill its slot kDepth units ahead. Past the
-    // end of the run a slot re-reads its own tile (a cache hit), so the loads stay
-    // unconditional.
+    // end of the run a slot re-reads the first row of its own tile (kIdleValid).
     uint32_t k0 = 0;
     for (; k0 + kDepth <= n; k0 += kDepth) {
       static_for<0, kDepth>([&](auto dc) {
@@ -999,6 +1011,7 @@ __device__ __forceinline__ void run_worker(const Args& a, const uint32_t* s_pre,
         const uint32_t k = k0 + d;
         process(k, rec[d], tiles[d]);
         if (k + kDepth < n) rec[d] = take();
+        else rec[d].valid = kIdleValid;
         P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
@@ -1387,7 +1400,7 @@ void seg_kernel(Args a) {
       r.ok = true;
       r.k = L.n;
       r.tile = last_tile;
-      r.valid = 0;
+      r.valid = kIdleValid;
       return r;
     }
     r.live = true;
@@ -1470,7 +1483,7 @@ void seg_kernel(Args a) {
   };
 
   // Consume the oldest unit, refill its slot kDepth units ahead. Past the end of the run a
-  // slot re-reads its last tile (a cache hit), so the loads stay unconditional.
+  // slot re-reads the first row of the last tile (kIdleValid).
   while (rec[0].live) {
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
@@ -1554,8 +1567,14 @@ void split_kernel(Args a) {
     typename P::TileT tiles[kDepth];
     static_for<0, kDepth>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      if constexpr (d == 0) rec[0] = take();
-      else rec[d] = static_cast<uint32_t>(d) < n ? take() : rec[d - 1];
+      if constexpr (d == 0) {
+        rec[0] = take();
+      } else if (static_cast<uint32_t>(d) < n) {
+        rec[d] = take();
+      } else {
+        rec[d] = rec[d - 1];
+        rec[d].valid = kIdleValid;
+      }
       P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
     });
     uint32_t k0 = 0;
@@ -1565,6 +1584,7 @@ void split_kernel(Args a) {
         bad |= !rec[d].ok;
         P::consume_unit(tiles[d], st, qh, a.scale_log2, lane, rec[d].valid);
         if (k0 + d + kDepth < n) rec[d] = take();
+        else rec[d].valid = kIdleValid;
         P::load(tiles[d], a, rec[d].tile, lane, rec[d].valid);
       });
     }
