@@ -880,6 +880,10 @@ COUNTER_PASSES = {
              "GRBM_GUI_ACTIVE"],   # SQ_ACTIVE_INST_VMEM reads 0 on gfx950
     "mem": ["TCC_HIT_sum", "TCC_MISS_sum", "TCP_UTCL1_TRANSLATION_MISS_sum",
             "TCP_UTCL1_TRANSLATION_HIT_sum", "TCP_TCC_READ_REQ_sum"],
+    # L2-to-memory read requests by size: FETCH_SIZE's expression counts a 128-byte request
+    # as 64 bytes on gfx950 (hence the copy calibration); these give the bytes directly.
+    "rdreq": ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
+              "TCC_EA0_RDREQ_sum"],
 }
 
 
@@ -1023,6 +1027,12 @@ def summarize_profile(d: str, tag: str):
         out.append(f"traffic_over_algorithmic: {traffic / alg:.4f}")
         out.append(f"achieved_gbs_at_trace_timed_avg: {alg / tavg:.1f}")
         out.append(f"frac_of_hbm_peak_at_trace_timed_avg: {alg / tavg / HBM_PEAK_GBS:.4f}")
+    rd = read_bytes_by_request_size(ctr)
+    if rd is not None:
+        wb = wa * write_scale * 1024
+        out.append(f"read_bytes_by_request_size_per_launch: {rd:.0f}")
+        out.append(f"read_plus_write_bytes_over_algorithmic: {(rd + wb) / alg:.4f}  "
+                   f"(cross-check of traffic_over_algorithmic without the copy calibration)")
     derived = derived_counters(ctr, tavg)
     if derived:
         out.append("")
@@ -1038,6 +1048,15 @@ def summarize_profile(d: str, tag: str):
 
 # MI355X: 256 compute units of 4 SIMDs in 8 XCDs; SQ cycle counters count quad-cycles.
 N_CU, N_SIMD, N_XCD, CLOCK_GHZ = 256, 1024, 8, 2.4
+
+
+def read_bytes_by_request_size(ctr):
+    """Bytes the L2 read from memory for one dispatch, from the request-size counters
+    (32, 64 and 128 bytes), or None where they were not collected."""
+    names = ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
+    if not all(n in ctr for n in names):
+        return None
+    return sum(size * _mean(ctr[n]) for size, n in zip((32, 64, 128), names))
 
 
 def derived_counters(ctr, kernel_ns):
@@ -1068,6 +1087,9 @@ def derived_counters(ctr, kernel_ns):
                   "SQ_INSTS_LDS", "SQ_INSTS_MFMA"):
             if k in m:
                 out.append((k.lower() + "_per_wave", f"{m[k] / m['SQ_WAVES']:.1f}"))
+    if m.get("TCC_EA0_RDREQ_sum"):
+        out.append(("share_of_128_byte_read_requests",
+                    f"{m.get('TCC_EA0_RDREQ_128B_sum', 0.0) / m['TCC_EA0_RDREQ_sum']:.4f}"))
     if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m and m["TCC_HIT_sum"] + m["TCC_MISS_sum"] > 0:
         out.append(("l2_hit_fraction", f"{m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.3f}"))
     if "TCP_UTCL1_TRANSLATION_MISS_sum" in m and "TCP_UTCL1_TRANSLATION_HIT_sum" in m:
