@@ -156,6 +156,34 @@ __device__ __forceinline__ float row_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one lane of each 16-lane row)
+// on the VALU: v_permlane16_swap of a value with itself leaves rows (0, 0, 2, 2) in one
+// result and (1, 1, 3, 3) in the other, v_permlane32_swap the halves (lo, lo) and (hi, hi).
+// Every lane of the four ends with the same bits. (A shuffle through ds_bpermute would wait
+// on the LDS queue, behind the operand reads in flight.) The two results are copied out
+// before any bit cast: a bit cast of an element of the returned pair read element 0.
+__device__ __forceinline__ float max_across_rows(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t w = __builtin_bit_cast(uint32_t, m);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float s = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  const uint32_t w = __builtin_bit_cast(uint32_t, s);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+
 __device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
 __device__ __forceinline__ bf2 as_bf2(uint32_t w) { return __builtin_bit_cast(bf2, w); }
 
@@ -619,8 +647,7 @@ __device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, c
     if constexpr (kMasked) sv[j] = 4 * q + j < valid ? sv[j] : kNegInf;
     mx = fmaxf(mx, sv[j]);
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_across_rows(mx);
   const bool grow = mx > st.m + kLazyRescale;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float m_new = grow ? mx : st.m;
@@ -684,9 +711,7 @@ template <int kGroup>
 __device__ __forceinline__ void mpublish(const MState& st, float* acc, float* m, float* l, int lane) {
   const int q = lane >> 4;
   const int n = lane & 15;
-  float sum = st.l;
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
+  const float sum = sum_across_rows(st.l);
   if (n < kGroup) {
     float* o = acc + n * kHeadDim + 32 * q;
 #pragma unroll
@@ -782,9 +807,7 @@ struct Path {
     if constexpr (kMf) {
       const int q = lane >> 4;
       const int n = lane & 15;
-      float sum = st.l;
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      const float sum = sum_across_rows(st.l);
       if (n < kGroup) {
         const float inv = 1.0f / sum;
         float* row = o + n * kHeadDim + 32 * q;

@@ -69,6 +69,34 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one lane of each 16-lane row)
+// on the VALU: v_permlane16_swap of a value with itself leaves rows (0, 0, 2, 2) in one
+// result and (1, 1, 3, 3) in the other, v_permlane32_swap the halves (lo, lo) and (hi, hi).
+// Every lane of the four ends with the same bits. (A shuffle through ds_bpermute would wait
+// on the LDS queue, behind the operand reads in flight.) The two results are copied out
+// before any bit cast: a bit cast of an element of the returned pair read element 0.
+__device__ __forceinline__ float max_across_rows_pf(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float m = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t w = __builtin_bit_cast(uint32_t, m);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+__device__ __forceinline__ float sum_across_rows_pf(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float s = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  const uint32_t w = __builtin_bit_cast(uint32_t, s);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t b0 = b[0], b1 = b[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
+
 // Read-only load through the scalar cache (constant address space), for values every lane
 // of the workgroup shares.
 __device__ __forceinline__ int32_t scalar_load_pf(const int32_t* base, int idx) {
@@ -442,8 +470,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[grp][sb][e]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_across_rows_pf(mx);
         mx *= ssc;
         const bool grow = mx > m[grp] + kLazyRescale;
         if (__ballot(grow)) {
@@ -487,9 +514,7 @@ void prefill_kernel(PrefillArgs a, int nx) {
     const float nan = __builtin_nanf("");
 #pragma unroll
     for (int grp = 0; grp < kRowGroups; ++grp) {
-      float lt = l[grp];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = sum_across_rows_pf(l[grp]);
       const int row = wrow0 + 16 * grp + col;
       if (row >= rows_total) continue;
       const float inv = 1.0f / lt;
