@@ -113,9 +113,11 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType k
   }
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
   // Segment mode needs a few segments per workgroup to balance whole segments, unless the
-  // caches are short.
+  // caches are short. The matrix-core builds take it from one segment per compute unit:
+  // there the balanced stream measured 13-40 % slower (its partial results and merge cost
+  // more than the imbalance of whole segments).
   const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * cus;
-  if (segments >= cus && (seg_balances || batch > dattn::kMaxBatch))
+  if (segments >= cus && (seg_balances || batch > dattn::kMaxBatch || dattn::use_mfma(kv, group)))
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   // Few segments over caches of at most kTinyCachePages: each workgroup's run is a few
   // round trips long, so partitions would only add the merge kernel.

@@ -218,10 +218,17 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=3).mode == binding.MODE_SEGMENT
     assert plan(lib, binding, 300, 8, 8, 4, cus=2).mode == binding.MODE_SEGMENT
     # Many pairs over long caches: segment mode while every workgroup gets two segments or
-    # more (1280 pairs, 256 workgroups for G = 4), else the balanced stream.
+    # more (1280 pairs, 256 workgroups for G = 4), else, for the vector-ALU builds (G <= 2,
+    # BF16), the balanced stream; the matrix-core builds keep segment mode from one pair per
+    # CU.
     assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 256
-    s3 = plan(lib, binding, 60, 256, 32, 8)
+    s3 = plan(lib, binding, 10, 256, 32, 32)
     assert s3.mode == binding.MODE_STREAM and s3.num_workgroups == 512
+    assert plan(lib, binding, 10, 256, 32, 32, kv=2).mode == binding.MODE_STREAM
+    m3 = plan(lib, binding, 60, 256, 32, 8)
+    assert (m3.mode, m3.num_workgroups) == (binding.MODE_SEGMENT, 256)
+    assert plan(lib, binding, 60, 256, 32, 8, kv=2).mode == binding.MODE_STREAM   # BF16, G = 4
+    assert plan(lib, binding, 40, 256, 64, 8, kv=3).mode == binding.MODE_SEGMENT  # FP8, G = 8
     # 64 x 8 pairs of G = 8 over 256-page INT8 caches (two pairs per CU): segment mode, with
     # the grid cut from the two workgroups per CU the build keeps resident to one, so that
     # each workgroup still gets two segments; 160 x 8 INT8 pairs keep both.
