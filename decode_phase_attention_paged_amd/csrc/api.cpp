@@ -113,21 +113,26 @@ dattn::Plan make_plan(int batch, int max_blocks, int n_kv_heads, dattn::KvType k
   }
   const long long segments = static_cast<long long>(batch) * n_kv_heads;
   // Segment mode needs a few segments per workgroup to balance whole segments, unless the
-  // caches are short. The matrix-core builds take it from one segment per compute unit:
-  // there the balanced stream measured 13-40 % slower (its partial results and merge cost
-  // more than the imbalance of whole segments).
+  // caches are short. Between one and two segments per compute unit only the 1-byte
+  // vector-ALU builds (G <= 2) keep the balanced stream: the others measured 5-40 % faster
+  // in segment mode (the stream's partial results and merge cost more than the imbalance
+  // of whole segments), the 1-byte ones 30-45 % slower (too few waves to hide latency).
   const bool seg_balances = max_blocks <= kShortCachePages || segments >= kMinSegmentsPerWorkgroup * cus;
-  if (segments >= cus && (seg_balances || batch > dattn::kMaxBatch || dattn::use_mfma(kv, group)))
+  const bool seg_preferred = dattn::use_mfma(kv, group) || dattn::kv_elem_bytes(kv) == 2;
+  if (segments >= cus && (seg_balances || batch > dattn::kMaxBatch || seg_preferred))
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   // Few segments over caches of at most kTinyCachePages: each workgroup's run is a few
   // round trips long, so partitions would only add the merge kernel.
   if (segments < cus && max_blocks <= kTinyCachePages)
     return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
   if (segments < cus) {
+    // Partitions for about kSplitWorkgroupsPerCu workgroups per CU, rounded to the nearest
+    // count; fewer than two (more than half as many segments as CUs) is segment mode, which
+    // measured faster than two partitions' one and a half rounds of workgroups.
     const long long want = static_cast<long long>(kSplitWorkgroupsPerCu) * cus;
-    const long long splits = segments > 0 ? (want + segments - 1) / segments : 1;
-    const dattn::Plan sp =
-        split_plan(batch, max_blocks, n_kv_heads, static_cast<int>(splits < 2 ? 2 : splits));
+    const long long splits = segments > 0 ? (want + segments / 2) / segments : 1;
+    if (splits < 2) return segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus);
+    const dattn::Plan sp = split_plan(batch, max_blocks, n_kv_heads, static_cast<int>(splits));
     return sp.num_splits == 1 ? segment_plan(batch, max_blocks, n_kv_heads, kv, group, 0, cus) : sp;
   }
   const long long max_units = segments * max_blocks;

@@ -218,17 +218,25 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     assert plan(lib, binding, 300, 8, 8, 1, cus=2, kv=3).mode == binding.MODE_SEGMENT
     assert plan(lib, binding, 300, 8, 8, 4, cus=2).mode == binding.MODE_SEGMENT
     # Many pairs over long caches: segment mode while every workgroup gets two segments or
-    # more (1280 pairs, 256 workgroups for G = 4), else, for the vector-ALU builds (G <= 2,
-    # BF16), the balanced stream; the matrix-core builds keep segment mode from one pair per
-    # CU.
+    # more (1280 pairs, 256 workgroups for G = 4); between one and two pairs per CU the
+    # 1-byte vector-ALU builds (G <= 2) take the balanced stream, every other build keeps
+    # segment mode.
     assert p3.mode == binding.MODE_SEGMENT and p3.num_workgroups == 256
-    s3 = plan(lib, binding, 10, 256, 32, 32)
+    s3 = plan(lib, binding, 10, 256, 32, 32, kv=1)
     assert s3.mode == binding.MODE_STREAM and s3.num_workgroups == 512
-    assert plan(lib, binding, 10, 256, 32, 32, kv=2).mode == binding.MODE_STREAM
+    assert plan(lib, binding, 10, 256, 32, 32, kv=3).mode == binding.MODE_STREAM
+    assert plan(lib, binding, 10, 256, 32, 32).mode == binding.MODE_SEGMENT        # fp16, G = 1
+    assert plan(lib, binding, 10, 256, 32, 32, kv=2).mode == binding.MODE_SEGMENT  # BF16, G = 1
     m3 = plan(lib, binding, 60, 256, 32, 8)
     assert (m3.mode, m3.num_workgroups) == (binding.MODE_SEGMENT, 256)
-    assert plan(lib, binding, 60, 256, 32, 8, kv=2).mode == binding.MODE_STREAM   # BF16, G = 4
     assert plan(lib, binding, 40, 256, 64, 8, kv=3).mode == binding.MODE_SEGMENT  # FP8, G = 8
+    # Fewer pairs than CUs over long caches: partitions for about one workgroup per CU,
+    # rounded; more than half as many pairs as CUs is segment mode.
+    assert plan(lib, binding, 24, 256, 32, 8).mode == binding.MODE_SEGMENT          # 192 pairs
+    p96 = plan(lib, binding, 12, 256, 32, 8)
+    assert (p96.mode, p96.num_splits) == (binding.MODE_SPLIT, 3)                     # 96 pairs
+    p32 = plan(lib, binding, 4, 256, 32, 8)
+    assert (p32.mode, p32.num_splits) == (binding.MODE_SPLIT, 8)                     # 32 pairs
     # 64 x 8 pairs of G = 8 over 256-page INT8 caches (two pairs per CU): segment mode, with
     # the grid cut from the two workgroups per CU the build keeps resident to one, so that
     # each workgroup still gets two segments; 160 x 8 INT8 pairs keep both.
