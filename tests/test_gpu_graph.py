@@ -209,16 +209,18 @@ def test_library_workspace_growth_keeps_earlier_graphs_valid(torch, lib):
         small_call()
     torch.cuda.synchronize()
 
-    big = Config(0, "g8_stream", batch=40, n_q_heads=64, n_kv_heads=8, head_dim=128,
-                 block_size=16, len_lo=1100, len_hi=2000, kv_dtype="fp16")
-    bp = lib.plan(big.batch, big.max_blocks_per_seq, big.n_q_heads, big.n_kv_heads, 16, "fp16",
+    # 320 (sequence, KV head) pairs of G = 2 over INT8 caches: the library plans stream mode,
+    # whose piece slots need more workspace than the small call's partitions.
+    big = Config(0, "int8_g2_stream", batch=40, n_q_heads=16, n_kv_heads=8, head_dim=128,
+                 block_size=16, len_lo=1100, len_hi=2000, kv_dtype="int8")
+    bp = lib.plan(big.batch, big.max_blocks_per_seq, big.n_q_heads, big.n_kv_heads, 16, "int8",
                   num_cus=cus)
     assert bp.mode == lib.MODE_STREAM and bp.workspace_bytes > p.workspace_bytes
     wb = generate(big, seed=96)
     db = to_dev(torch, wb)
     print("case workspace growth: large stream call", flush=True)
     big_out = lib.decode_attn(db["q"], db["k_pages"], db["v_pages"], db["block_table"],
-                              db["seq_lens"], wb.scale)
+                              db["seq_lens"], wb.scale, k_scale=db["k_scale"], v_scale=db["v_scale"])
     torch.cuda.synchronize()
     assert_parity(big_out.cpu().numpy(), oracle_run(wb)[0], "large call that grew the workspace")
     junk = torch.full((64 << 20,), 0x7F, dtype=torch.uint8, device="cuda:0")
