@@ -1025,6 +1025,12 @@ def summarize_profile(d: str, tag: str):
         out.append(f"algorithmic_bytes_per_launch: {alg}")
         out.append(f"traffic_bytes_per_launch: {traffic:.0f}")
         out.append(f"traffic_over_algorithmic: {traffic / alg:.4f}")
+        if op == "attn" and "kv_bytes_per_step" in cfg:
+            # The K/V reads are the throughput figure's bytes; the step also reads q (16-bit)
+            # and writes out (fp32), which the traffic counters see.
+            qo = cfg["batch"] * cfg["n_q_heads"] * cfg["head_dim"] * (2 + 4)
+            out.append(f"traffic_over_kv_plus_q_and_out: {traffic / (alg + qo):.4f}  "
+                       f"(q 16-bit and out fp32: {qo} bytes)")
         out.append(f"achieved_gbs_at_trace_timed_avg: {alg / tavg:.1f}")
         out.append(f"frac_of_hbm_peak_at_trace_timed_avg: {alg / tavg / HBM_PEAK_GBS:.4f}")
     rd = read_bytes_by_request_size(ctr)

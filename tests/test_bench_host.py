@@ -80,7 +80,8 @@ def test_summarize_profile_on_synthetic_output(tmp_path, monkeypatch):
     alg = 1_500_000
     rec = {"metric": bench.METRIC, "argv": ["--config", "2"], "steps": 2, "repeats": 1,
            "us_per_step": 1.0,
-           "config": {"workload": "synthetic_case", "kv_bytes_per_step": alg}}
+           "config": {"workload": "synthetic_case", "kv_bytes_per_step": alg, "batch": 2,
+                      "n_q_heads": 4, "head_dim": 128}}
     d.mkdir()
     (d / f"trace_{tag}.json").write_text("progress line\n" + json.dumps(rec) + "\n")
     trace = [{"Kernel_Name": kernel, "Start_Timestamp": 100 * i, "End_Timestamp": 100 * i + 1000,
@@ -120,6 +121,9 @@ def test_summarize_profile_on_synthetic_output(tmp_path, monkeypatch):
     assert float(fields["read_bytes_by_request_size_per_launch"]) == pytest.approx(2_000_000)
     assert float(fields["read_plus_write_bytes_over_algorithmic"].split()[0]) == pytest.approx(
         2_500_000 / alg, abs=1e-4)
+    qo = 2 * 4 * 128 * (2 + 4)
+    assert float(fields["traffic_over_kv_plus_q_and_out"].split()[0]) == pytest.approx(
+        2_500_000 / (alg + qo), abs=1e-4)
     # 1.5 MB in 1000 ns = 1500 GB/s.
     assert float(fields["achieved_gbs_at_trace_timed_avg"]) == pytest.approx(1500.0)
     assert fields["kernel_source_sha256"] == bench.kernel_source_hash(bench.SOURCES_OF_OP["attn"])
