@@ -940,11 +940,13 @@ def summarize_profile(d: str, tag: str):
         res[name] = (r.get("VGPR_Count"), r.get("Accum_VGPR_Count"), r.get("SGPR_Count"),
                      r.get("LDS_Block_Size"), r.get("Scratch_Size"), r.get("Grid_Size_X"),
                      r.get("Workgroup_Size_X"))
+    # The counter passes of this tag only: pmc_<pass>_<tag> for the known pass names (a
+    # suffix match would also take, say, pmc_FETCH_SIZE_append_cfg2 for tag cfg2).
     passes = {}
-    for name in sorted(os.listdir(d)):
-        full = os.path.join(d, name)
-        if name.startswith("pmc_") and name.endswith("_" + tag) and os.path.isdir(full):
-            passes[name[4:-len(tag) - 1]] = _pmc(full)
+    for pname in ["FETCH_SIZE", "WRITE_SIZE", *COUNTER_PASSES]:
+        full = os.path.join(d, f"pmc_{pname}_{tag}")
+        if os.path.isdir(full):
+            passes[pname] = _pmc(full)
 
     def counters_of(kernel):
         merged = {}

@@ -104,6 +104,9 @@ def test_summarize_profile_on_synthetic_output(tmp_path, monkeypatch):
                _pmc_rows(kernel, [{"TCC_EA0_RDREQ_32B_sum": 0.0, "TCC_EA0_RDREQ_64B_sum": 0.0,
                                    "TCC_EA0_RDREQ_128B_sum": 2_000_000 / 128,
                                    "TCC_EA0_RDREQ_sum": 2_000_000 / 128}] * 2))
+    # Another workload's passes in the same directory, whose tag ends like this one's.
+    _write_csv(str(d / f"pmc_FETCH_SIZE_append_{tag}" / "run_counter_collection.csv"),
+               _pmc_rows("void dattn::append_kernel(dattn::AppendArgs)", [{"FETCH_SIZE": 1.0}]))
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     bench.summarize_profile(str(d), tag)
     text = (tmp_path / "decode_attn_synthetic_case.txt").read_text()
@@ -112,6 +115,8 @@ def test_summarize_profile_on_synthetic_output(tmp_path, monkeypatch):
         if ": " in line and not line.startswith("#") and not line.startswith(" "):
             k, v = line.split(": ", 1)
             fields[k] = v
+    assert "command_pmc_FETCH_SIZE_append" not in fields
+    assert "command_pmc_rdreq" in fields
     assert fields["dominant_kernel"] == kernel
     assert float(fields["dominant_kernel_timed_avg_ns"]) == 1000.0
     assert float(fields["fetch_scale"]) == pytest.approx(2.0)
