@@ -149,6 +149,26 @@ def test_edge_lengths_and_nan_canaries(torch, lib, kv):
         assert np.all(got[lens == 0] == 0)
 
 
+@pytest.mark.parametrize("kv,group", [("fp16", 1), ("fp16", 2), ("int8", 4), ("fp8", 8)])
+def test_segment_mode_full_and_partial_rounds(torch, lib, kv, group):
+    # 160 segments dealt in a snake over grids that leave the last round full, partial or a
+    # single segment, and over one round; lengths from a small set (ties, empty caches).
+    n_kv = 4
+    cfg = SMALL.with_(kv_dtype=kv, batch=40, n_q_heads=n_kv * group, n_kv_heads=n_kv,
+                      len_lo=0, len_hi=700)
+    rng = np.random.default_rng(40 + group)
+    lens = rng.choice(np.array([0, 1, 16, 17, 64, 65, 300, 700], dtype=np.int32), size=cfg.batch)
+    w = generate(cfg, seed=41, seq_lens=lens, extra_pages=2, poison=True)
+    print(f"case segment rounds kv={kv} G={group}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    d = to_dev(torch, w)
+    for grid in (3, 7, 31, 53, 80, 159, 160, 161):
+        got, lse = gpu_run(torch, lib, w, dev_inputs=d, num_splits=1, num_workgroups=grid)
+        assert np.isfinite(got).all(), f"grid {grid}: a NaN canary leaked into the output"
+        assert_parity(got, ref, f"segment rounds {kv} G={group} grid {grid}")
+        assert_lse(lse, ref_lse, "lse")
+
+
 @pytest.mark.parametrize("batch", [255, 256, 257])
 @pytest.mark.parametrize("grid", [0, 3, 1000])
 @pytest.mark.parametrize("caches", ["short", "long"])
