@@ -160,17 +160,19 @@ int decode_attn(const void* q, const void* k_pages, const void* v_pages,
  * Planning (swiftLLM feature list: Flash-Decoding). The requests:
  *  - requested_splits == 1: segment mode, on requested_workgroups workgroups if that is
  *    > 0, else on as many as stay resident on num_cus compute units (never more than
- *    batch * n_kv_heads);
+ *    batch * n_kv_heads, and over caches of more than 64 pages no more than one per two
+ *    pairs unless that is below num_cus);
  *  - requested_splits > 1 (requested_workgroups must be 0): split mode with that many page
  *    partitions per (sequence, KV head); the result may be smaller, namely
  *    ceil(max_blocks_per_seq / ceil(max_blocks_per_seq / requested_splits)), and a result
  *    of 1 is segment mode;
  *  - requested_workgroups > 0 alone: stream mode on that many workgroups;
- *  - both 0: the library's choice from the shapes and num_cus: with fewer (sequence, KV
- *    head) pairs than compute units, segment mode for caches of at most 16 pages and split
- *    mode otherwise; with more, segment mode when caches are at most 64 pages, when there
- *    are at least two pairs per segment-mode workgroup, or when the batch exceeds 4096
- *    sequences, and stream mode otherwise.
+ *  - both 0: the library's choice from the shapes, the format, G and num_cus. With fewer
+ *    (sequence, KV head) pairs than compute units: segment mode for caches of at most 16
+ *    pages, else split mode with num_cus / pairs partitions rounded to the nearest (segment
+ *    mode when that is below 2). With more: segment mode when caches are at most 64 pages,
+ *    when there are at least two pairs per compute unit, when the batch exceeds 4096
+ *    sequences, or for every build but INT8 and FP8 with G <= 2; stream mode otherwise.
  * num_cus is the device's compute-unit count; 0 queries the current device (the only HIP
  * call, made only when the plan needs the count). kv_dtype is a decode_attn_kv_dtype (the
  * grid of segment mode depends on it). Fills *plan and returns a decode_attn_status.
