@@ -324,6 +324,56 @@ def test_page_permutation_is_bitwise_invariant(torch, lib, plan):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("group", [1, 4, 8])
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 2.0])
+def test_softmax_scale_extremes(torch, lib, kv, group, scale):
+    """A negative scale (the smallest products get the largest weights), a zero scale (the
+    mean of V) and a sharp one (near one-hot weights), on both consumes (vector G = 1,
+    matrix cores G >= 4 over fp16, INT8, FP8) and every plan kind."""
+    cfg = SMALL.with_(kv_dtype=kv, n_q_heads=2 * group, n_kv_heads=2, len_lo=1, len_hi=400)
+    w = generate(cfg, seed=50 + group)
+    w.scale = float(np.float32(scale))
+    print(f"case scale {scale} kv={kv} G={group}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    d = to_dev(torch, w)
+    for plan in (dict(num_splits=1), dict(num_workgroups=3), dict(num_splits=3)):
+        got, lse = gpu_run(torch, lib, w, dev_inputs=d, **plan)
+        assert_parity(got, ref, f"scale {scale} {kv} G={group} {plan}")
+        assert_lse(lse, ref_lse, "lse")
+
+
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("group", [1, 4, 8])
+def test_running_max_rises_every_page(torch, lib, kv, group):
+    """Scores that grow along each cache (key t = (t / 64) u, with every query head equal
+    to u), so the running max keeps moving: by about 4 log2 units per page, past the matrix-
+    core consume's lazy threshold every two pages; the weights end up on the last few
+    tokens."""
+    cfg = SMALL.with_(kv_dtype=kv, n_q_heads=2 * group, n_kv_heads=2, len_lo=200, len_hi=400)
+    w = generate(cfg, seed=70 + group)
+    rng = np.random.default_rng(71)
+    u = rng.standard_normal(128).astype(np.float32)
+    w.q[...] = u.astype(np.float16)
+    bs = cfg.block_size
+    for b in range(cfg.batch):
+        for t in range(int(w.seq_lens[b])):
+            page, slot = int(w.block_table[b, t // bs]), t % bs
+            c = t / 64.0
+            if kv == "fp16":
+                w.k_pages[page, :, slot, :] = (c * u).astype(np.float16)
+            else:
+                w.k_pages[page, :, slot, :] = np.clip(np.rint(u * 30.0), -127, 127).astype(np.int8)
+                w.k_scale[page, :, slot] = np.float32(c / 30.0)
+    print(f"case rising max kv={kv} G={group}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    d = to_dev(torch, w)
+    for plan in (dict(num_splits=1), dict(num_workgroups=3), dict(num_splits=3)):
+        got, lse = gpu_run(torch, lib, w, dev_inputs=d, **plan)
+        assert_parity(got, ref, f"rising max {kv} G={group} {plan}")
+        assert_lse(lse, ref_lse, "lse")
+
+
 def test_gqa_matches_repeated_mha(torch, lib):
     """G = 4 against the same heads as MHA (K/V repeated per query head). The G = 4 build
     runs on the matrix cores, which take each softmax weight rounded to fp16 (relative error
