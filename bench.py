@@ -279,7 +279,8 @@ def main():
                     help="capture this many consecutive steps in one HIP graph and time "
                          "replays of it (the step count is rounded up to a multiple)")
     ap.add_argument("--kv", choices=["fp16", "bf16", "int8", "fp8"], default=None,
-                    help="prefill only: run the preset's shapes over another storage format")
+                    help="run the preset's shapes over another storage format (the workload "
+                         "name gets the format as a suffix)")
     ap.add_argument("--op", choices=["attn", "append", "prefill", "step"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
                          "that precedes it in a decode step, on the same workload; step: "
@@ -294,8 +295,6 @@ def main():
             ap.error("--summarize-profile needs --tag")
         summarize_profile(args.summarize_profile, args.tag)
         return
-    if args.kv is not None and args.op != "prefill":
-        ap.error("--kv applies to --op prefill only; the decode presets fix their formats")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this library runs decode attention on a single "
@@ -318,6 +317,8 @@ def main():
     if args.config == 0:
         args.config = DEFAULT_CONFIG[args.op]
     cfg = CONFIGS[args.config]
+    if args.kv and args.kv != cfg.kv_dtype:
+        cfg = cfg.with_(kv_dtype=args.kv, name=f"{cfg.name}_{args.kv}")
     if args.op == "append":
         return bench_append(args, cfg, lib, torch, np, binding, generate)
     if args.op == "prefill":

@@ -34,15 +34,15 @@ enum class Mode { kStream = 0, kSplit = 1, kSegment = 2 };
 
 constexpr int log2_group(int g) { return g == 1 ? 0 : g == 2 ? 1 : g == 4 ? 2 : 3; }
 
-// Builds whose tile products run on the matrix cores: G >= 4 over fp16, INT8 and FP8. Their
-// work per tile does not depend on G, so their tuning is one entry per element width
-// (index 0: 2-byte, 1: 1-byte); the vector-ALU builds are tuned per width and log2 G.
-constexpr bool use_mfma(KvType kv, int group) { return group >= 4 && kv != KvType::kBF16; }
+// Builds whose tile products run on the matrix cores: G >= 4, every format. Their work per
+// tile does not depend on G, so their tuning is one entry per element width (index 0:
+// 2-byte, 1: 1-byte); the vector-ALU builds (G <= 2) are tuned per width and log2 G.
+constexpr bool use_mfma(KvType kv, int group) { return (void)kv, group >= 4; }
 constexpr int width_index(KvType kv) { return kv_elem_bytes(kv) == 2 ? 0 : 1; }
 
 // Waves per SIMD the segment-mode kernel is compiled for; the host sizes that mode's grid
 // to the workgroups that stay resident at that occupancy.
-constexpr int kSegWavesF16[4] = {1, 2, 1, 1};   // fp16 G <= 2, bf16
+constexpr int kSegWavesF16[2] = {1, 2};         // fp16 and BF16, G <= 2
 constexpr int kSegWavesI8[2] = {3, 2};          // INT8 and FP8, G <= 2
 constexpr int kSegWavesMf[2] = {1, 2};
 constexpr int seg_waves(KvType kv, int group) {

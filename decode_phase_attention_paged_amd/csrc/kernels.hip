@@ -59,8 +59,8 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 //       the contiguous bytes [1024 i, 1024 i + 1024), lane l at byte 16 l.
 // int8: a row is 128 B = 8 lanes of 16 B; lane row r covers tokens 2r and 2r + 1 (loads 0
 //       and 1) so that its two row scales are one 8-byte load.
-// bf16 takes the fp16 geometry and fp8 the int8 one. These are the vector-ALU builds; G >= 4
-// over fp16, INT8 and FP8 runs on the matrix cores with its own layout (below).
+// bf16 takes the fp16 geometry and fp8 the int8 one. These are the vector-ALU builds (G <= 2);
+// G >= 4 runs on the matrix cores with its own layout (below).
 template <KvType kKv, int kGroup>
 struct Geo {
   static constexpr int kElem = kv_elem_bytes(kKv);
@@ -87,32 +87,30 @@ struct Geo {
 };
 
 // Tuning per kernel: units kept in flight per wave, and the waves per SIMD the kernel is
-// compiled for (which caps its VGPRs at 512 / waves). Vector-ALU builds are indexed by
-// log2 G (a larger group holds more accumulators, so it keeps fewer tiles); the 1-byte
-// tables stop at G = 2 because G >= 4 over 1-byte formats runs on the matrix cores, whose
-// tables are indexed by element width (0: 2-byte, 1: 1-byte).
-constexpr int kStreamDepthF16[4] = {4, 4, 3, 2};
+// compiled for (which caps its VGPRs at 512 / waves). Vector-ALU builds (G <= 2) are
+// indexed by log2 G; the matrix-core builds (G >= 4) by element width (0: 2-byte, 1: 1-byte).
+constexpr int kStreamDepthF16[2] = {4, 4};
 constexpr int kStreamDepthI8[2] = {6, 4};
 constexpr int kStreamDepthMf[2] = {3, 3};
-constexpr int kStreamWavesF16[4] = {2, 2, 2, 1};
+constexpr int kStreamWavesF16[2] = {2, 2};
 constexpr int kStreamWavesI8[2] = {2, 2};
 constexpr int kStreamWavesMf[2] = {2, 1};
 // Split mode runs a few long partitions per sequence, about one workgroup per CU, so each
 // wave keeps many tiles in flight.
-constexpr int kSplitDepthF16[4] = {4, 4, 3, 2};
+constexpr int kSplitDepthF16[2] = {4, 4};
 constexpr int kSplitDepthI8[2] = {6, 4};
 constexpr int kSplitDepthMf[2] = {3, 3};
-constexpr int kSplitWavesF16[4] = {1, 1, 1, 1};
+constexpr int kSplitWavesF16[2] = {1, 1};
 constexpr int kSplitWavesI8[2] = {1, 1};
 constexpr int kSplitWavesMf[2] = {1, 1};
 // Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
 // Many resident workgroups with shallow rings measured faster than deep rings.
-constexpr int kSegDepthF16[4] = {2, 2, 2, 2};
+constexpr int kSegDepthF16[2] = {2, 2};
 constexpr int kSegDepthI8[2] = {1, 3};
 constexpr int kSegDepthMf[2] = {2, 2};
 
 template <KvType kKv, int kGroup>
-constexpr int pick(const int (&f16)[4], const int (&i8)[2], const int (&mf)[2]) {
+constexpr int pick(const int (&f16)[2], const int (&i8)[2], const int (&mf)[2]) {
   return use_mfma(kKv, kGroup)       ? mf[width_index(kKv)]
          : kv_elem_bytes(kKv) == 2 ? f16[log2_group(kGroup)]
                                    : i8[log2_group(kGroup)];
@@ -512,10 +510,15 @@ __device__ __forceinline__ void merge_rows(State<kKv, kGroup>& st) {
 // and the running max moves only when a tile exceeds it by more than kLazyRescale (log2
 // units), so most tiles skip the rescale and the weights, rounded to fp16 for the matrix
 // cores, stay below 2^8. INT8 and FP8 codes are widened exactly to fp16 (as in the vector
-// path); a row's K scale multiplies its score and its V scale its weight. BF16 caches keep
-// the vector path (bf16 weights would lose precision, see the chunked-prefill kernel).
+// path); a row's K scale multiplies its score and its V scale its weight. BF16 caches run
+// the bf16 shapes (v_mfma_f32_16x16x32_bf16, v_mfma_f32_16x16x16_bf16): the scores take
+// bf16 q and K (exact products, as in the vector path), and each weight enters the weighted
+// sum as two bf16 parts, hi = bf16(p) and lo = bf16(p - hi), in two products, since one
+// bf16 weight would carry errors up to 2^-8 of a value (the two parts keep 2^-16).
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLazyRescale = 8.0f;
@@ -586,10 +589,10 @@ __device__ __forceinline__ void mload_tile(MTile<kKv>& t, const Args& a, uint32_
   }
 }
 
-// Eight K values of score step s as an fp16 operand.
+// Eight K values of score step s as an fp16 operand (the raw bf16 bits for a BF16 cache).
 template <KvType kKv>
 __device__ __forceinline__ h8 mk_operand(const MTile<kKv>& t, int s) {
-  if constexpr (kKv == KvType::kF16) {
+  if constexpr (kv_elem_bytes(kKv) == 2) {
     return __builtin_bit_cast(h8, t.k[s]);
   } else {
     const u32x4 w = t.k[s >> 1];
@@ -607,12 +610,13 @@ __device__ __forceinline__ h8 mk_operand(const MTile<kKv>& t, int s) {
   }
 }
 
-// The four V rows of the lane as fp16 words (word w of row j holds d = 8m + 2w, 8m + 2w + 1).
+// The four V rows of the lane as 16-bit words (word w of row j holds d = 8m + 2w, 8m + 2w + 1):
+// fp16, or the raw bf16 of a BF16 cache.
 template <KvType kKv>
 __device__ __forceinline__ void mv_words(const MTile<kKv>& t, u32x4 (&v)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    if constexpr (kKv == KvType::kF16) {
+    if constexpr (kv_elem_bytes(kKv) == 2) {
       v[j] = t.v[j];
     } else {
       h2 x[4];
@@ -635,8 +639,13 @@ __device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, c
   const int q = lane >> 4;
   f4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(mk_operand<kKv>(t, s), qm.s[s], sc, 0, 0, 0);
+  for (int s = 0; s < 4; ++s) {
+    if constexpr (kKv == KvType::kBF16)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, mk_operand<kKv>(t, s)),
+                                                  __builtin_bit_cast(b8, qm.s[s]), sc, 0, 0, 0);
+    else
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(mk_operand<kKv>(t, s), qm.s[s], sc, 0, 0, 0);
+  }
   float sv[4];
   float mx = kNegInf;
 #pragma unroll
@@ -658,7 +667,7 @@ __device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, c
     st.m = m_new;
   }
   const float base = st.m == kNegInf ? 0.0f : st.m;
-  h4 pw;
+  float pf[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float p = fast_exp2(sv[j] - base);
@@ -667,7 +676,18 @@ __device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, c
       const bool ok = !kMasked || 4 * q + j < valid;
       p *= ok ? t.vs[j] : 0.0f;
     }
-    pw[j] = static_cast<_Float16>(p);
+    pf[j] = p;
+  }
+  h4 pw;     // fp16 weights; for BF16, the two bf16 parts
+  b4 pw_hi, pw_lo;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (kKv == KvType::kBF16) {
+      pw_hi[j] = static_cast<__bf16>(pf[j]);
+      pw_lo[j] = static_cast<__bf16>(pf[j] - static_cast<float>(pw_hi[j]));
+    } else {
+      pw[j] = static_cast<_Float16>(pf[j]);
+    }
   }
   u32x4 v[4];
   mv_words<kKv>(t, v);
@@ -678,8 +698,14 @@ __device__ __forceinline__ void mconsume_tile(const MTile<kKv>& t, MState& st, c
     const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
     const uint32_t lo = __builtin_amdgcn_perm(v[1][b >> 1], v[0][b >> 1], sel);
     const uint32_t hi = __builtin_amdgcn_perm(v[3][b >> 1], v[2][b >> 1], sel);
-    const h4 va = __builtin_bit_cast(h4, u32x2{lo, hi});
-    st.o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pw, st.o[b], 0, 0, 0);
+    if constexpr (kKv == KvType::kBF16) {
+      const b4 va = __builtin_bit_cast(b4, u32x2{lo, hi});
+      st.o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pw_hi, st.o[b], 0, 0, 0);
+      st.o[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pw_lo, st.o[b], 0, 0, 0);
+    } else {
+      const h4 va = __builtin_bit_cast(h4, u32x2{lo, hi});
+      st.o[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pw, st.o[b], 0, 0, 0);
+    }
   }
 }
 
@@ -731,8 +757,8 @@ __device__ __forceinline__ void store_chunk(float* dst, const float* src, int n)
     *reinterpret_cast<float4*>(dst + j) = make_float4(src[j], src[j + 1], src[j + 2], src[j + 3]);
 }
 
-// The tile consume a (G, format) build takes in every mode: the matrix cores
-// for G >= 4 over fp16, INT8 and FP8, the vector ALU otherwise.
+// The tile consume a (G, format) build takes in every mode: the matrix cores for G >= 4, the
+// vector ALU otherwise.
 template <KvType kKv, int kGroup>
 struct Path {
   static constexpr bool kMf = use_mfma(kKv, kGroup);

@@ -33,11 +33,11 @@
  * Each only changes the order of rounding; out is the plain softmax result above.
  *
  * Precision: scores, the running max and sum, and all accumulators are fp32. With G >= 4
- * query heads per KV head over fp16, INT8 or FP8 caches, both products of a page run on the
- * matrix cores: the scores as exact fp16 products (codes widened exactly) summed in fp32,
- * the weighted sum of V with each softmax weight rounded to fp16 (relative error at most
- * 2^-11; the normaliser adds the unrounded fp32 weights). With G <= 2, and for BF16 caches,
- * the weights stay fp32.
+ * query heads per KV head both products of a page run on the matrix cores: the scores as
+ * exact fp16 products (codes widened exactly; bf16 products for a BF16 cache) summed in
+ * fp32, the weighted sum of V with each softmax weight rounded to fp16 (relative error at
+ * most 2^-11), or for a BF16 cache split into two bf16 parts (at most 2^-16); the
+ * normaliser adds the unrounded fp32 weights. With G <= 2 the weights stay fp32.
  *
  * Memory layout (all row-major and contiguous; all tensor pointers are DEVICE pointers
  * owned by the caller, for example torch tensors; the library never frees them):
