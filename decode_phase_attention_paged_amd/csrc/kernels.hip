@@ -3,15 +3,17 @@
 // A unit is one (sequence b, KV head g, logical page j): the 16 tokens of one KV head in
 // one page, i.e. one K tile and one V tile (4 KiB each in fp16). A segment is the run of
 // units of one (b, g) pair. Every kernel here streams units from HBM straight into VGPRs
-// with 16-byte loads (one wave load covers 1 KiB of a tile with no gaps), keeps several
-// units in flight per wave, scores each tile against all G query heads sharing the KV
-// head (GQA, xLLM README optimisation list), finishes the dot products with DPP reductions
-// inside each token row of 16 lanes (fp16) or 8 lanes (int8), and folds the scores into a
-// running max / running sum softmax per lane row (the online normaliser of the xLLM README
-// SoftMax operator). Where a segment is cut between workers, the pieces leave partial
-// (output, log-sum-exp) pairs that a second kernel merges by their log-sum-exp weights in
-// a fixed order (PagedAttention v2 / Flash-Decoding, swiftLLM feature list). No atomics
-// anywhere, so a given plan gives bitwise-identical results.
+// with 16-byte non-temporal loads, keeps several units in flight per wave, and scores each
+// tile against all G query heads sharing the KV head (GQA, xLLM README optimisation list),
+// folding the scores into a running max / running sum softmax (the online normaliser of
+// the xLLM README SoftMax operator). Two tile consumes exist: with G <= 2 the vector ALU
+// (dot products finished with DPP reductions inside each token row of 16 lanes for 16-bit
+// formats, 8 for 1-byte ones); with G >= 4 the matrix cores, the G heads as the N columns
+// of 16x16 MFMA tiles for both the scores and the weighted sum. Where a segment is cut
+// between workers, the pieces leave partial (output, log-sum-exp) pairs that a second
+// kernel merges by their log-sum-exp weights in a fixed order (PagedAttention v2 /
+// Flash-Decoding, swiftLLM feature list). No atomics anywhere, so a given plan gives
+// bitwise-identical results.
 //
 // Three ways of cutting the batch into work:
 //  * segment mode: a fixed grid of persistent workgroups takes whole segments, longest
@@ -19,14 +21,17 @@
 //    states in LDS, so nothing is cut and no second kernel runs. Used for most batches.
 //  * stream mode: a fixed grid of persistent workgroups; units are numbered b-major, then
 //    g, then j, and wavefront w of W takes units [w T / W, (w + 1) T / W) of the T units.
-//    Every wave streams the same number of pages whatever the mix of lengths. Used when
-//    segments are too few or too long to balance whole.
+//    Every wave streams the same number of pages whatever the mix of lengths. The
+//    library's choice only for 1-byte caches with G <= 2 and one to two segments per
+//    compute unit over long caches.
 //  * split mode: one workgroup per (page partition, g, b), its four waves interleaving the
-//    partition's pages and merging in LDS. Used for a few very long caches.
+//    partition's pages and merging in LDS. Used for fewer segments than compute units over
+//    long caches.
 //
 // The path is bound by HBM bandwidth: per token and KV head it reads 2 * 128 * 2 bytes
 // (fp16) for 4 * G * 128 flops, far below the VALU or MFMA ridge point, so the design
-// spends its effort on keeping loads in flight, not on matrix cores. The only vector
+// spends its effort on keeping loads in flight; the matrix cores take the tile products
+// only where G made the vector ALU work per byte large enough to matter. The only vector
 // memory operations inside the streaming loops are the tile loads: page ids come through
 // scalar loads (or LDS) and query rows from LDS, so the compiler can wait for exactly the
 // oldest tile and leave the newer ones in flight.
@@ -104,7 +109,8 @@ constexpr int kSplitWavesF16[2] = {1, 1};
 constexpr int kSplitWavesI8[2] = {1, 1};
 constexpr int kSplitWavesMf[2] = {1, 1};
 // Segment mode (waves per SIMD in kSegWaves*, kernels.h, which the host plan also reads).
-// Many resident workgroups with shallow rings measured faster than deep rings.
+// Shallow rings (one or two units in flight per wave) measured faster than deep ones: with
+// about 16 MB of tiles in flight over the chip, more only lengthens the memory queue.
 constexpr int kSegDepthF16[2] = {2, 2};
 constexpr int kSegDepthI8[2] = {1, 3};
 constexpr int kSegDepthMf[2] = {2, 2};
