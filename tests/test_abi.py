@@ -230,6 +230,7 @@ def test_auto_plan_for_the_preset_shapes(lib, binding):
     m3 = plan(lib, binding, 60, 256, 32, 8)
     assert (m3.mode, m3.num_workgroups) == (binding.MODE_SEGMENT, 256)
     assert plan(lib, binding, 40, 256, 64, 8, kv=3).mode == binding.MODE_SEGMENT  # FP8, G = 8
+    assert plan(lib, binding, 60, 256, 32, 8, kv=2).mode == binding.MODE_SEGMENT  # BF16, G = 4
     # Fewer pairs than CUs over long caches: partitions for about one workgroup per CU,
     # rounded; more than half as many pairs as CUs is segment mode.
     assert plan(lib, binding, 24, 256, 32, 8).mode == binding.MODE_SEGMENT          # 192 pairs
