@@ -65,14 +65,40 @@ PREFIX_OF_OP = {"attn": "decode_attn", "append": "decode_attn_append",
                 "prefill": "decode_attn_prefill", "step": "decode_attn_step"}
 
 
+def strip_comments(text: str) -> str:
+    """C++ source without its comments and blank lines, trailing spaces trimmed; string and
+    character literals are kept whole (a // inside one is not a comment)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            end = text.find("*/", i + 2)
+            i = n if end < 0 else end + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_hash(sources=ATTN_SOURCES) -> str:
     """Hash of the sources that decide what a kernel does (the kernel file, the internal
-    interface and the host side that plans and launches it)."""
+    interface and the host side that plans and launches it), without their comments: an
+    edit of a comment leaves the compiled kernels, and so the profiles, as they were."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_phase_attention_paged_amd", "csrc")
     for name in sources:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

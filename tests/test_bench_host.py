@@ -134,6 +134,16 @@ def test_summarize_profile_on_synthetic_output(tmp_path, monkeypatch):
     assert fields["kernel_source_sha256"] == bench.kernel_source_hash(bench.SOURCES_OF_OP["attn"])
 
 
+def test_source_hash_ignores_comments_only():
+    code = 'int f(int x) {  // doubled\n  return 2 * x; /* no overflow\n here */\n}\n'
+    same = '/* header */\nint f(int x) {\n\n  return 2 * x;   // other words\n}\n'
+    other = 'int f(int x) {\n  return 3 * x;\n}\n'
+    assert bench.strip_comments(code) == bench.strip_comments(same)
+    assert bench.strip_comments(code) != bench.strip_comments(other)
+    assert bench.strip_comments('const char* s = "a // b"; char c = \'/\';') == \
+        'const char* s = "a // b"; char c = \'/\';'
+
+
 def test_build_reads_scratch_from_resource_remarks():
     remarks = "\n".join([
         "kernels.hip:10:1: remark: Function Name: _Z3fooPf [-Rpass-analysis=kernel-resource-usage]",
