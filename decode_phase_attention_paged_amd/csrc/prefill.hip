@@ -320,12 +320,14 @@ void prefill_kernel(PrefillArgs a, int nx) {
     u32x4 kr[4], vr[4];
     u32x2 kc[4], vcode[4];
     float ksc[4], vsc[4];
-    auto fetch = [&](int j) __attribute__((always_inline)) {
-      const int last_slot = (L - 1) % kBlockSize;
-      // Page ids of the tile's four pages: uniform, through the scalar cache.
-      int phys[kPagesPerTile];
+    // Page ids of tile j's four pages: uniform, through the scalar cache (clamped to the
+    // last page, so every index is valid for any j once nb > 0).
+    auto page_ids = [&](int j, int* phys) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < kPagesPerTile; ++i) phys[i] = scalar_load_pf(table, min(kPagesPerTile * j + i, nb - 1));
+    };
+    auto fetch = [&](int j, const int* phys) __attribute__((always_inline)) {
+      const int last_slot = (L - 1) % kBlockSize;
 #pragma unroll
       for (int i = 0; i < kPagesPerTile; ++i) {
         const int t = (kPagesPerTile * j + i) * kBlockSize + st;
@@ -371,9 +373,17 @@ void prefill_kernel(PrefillArgs a, int nx) {
         }
       }
     };
-    if (tiles > 0) fetch(0);
+    if (tiles > 0) {
+      int phys[kPagesPerTile];
+      page_ids(0, phys);
+      fetch(0, phys);
+    }
     for (int j = 0; j < tiles; ++j) {
       __syncthreads();   // the previous tile is no longer read
+      // The next tile's page ids are requested before the staging, so their latency
+      // overlaps it instead of delaying the tile loads below.
+      int next[kPagesPerTile];
+      page_ids(j + 1, next);
       if constexpr (kCodes) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -395,17 +405,16 @@ void prefill_kernel(PrefillArgs a, int nx) {
       for (int x = 0; x < 8; ++x) {
         const int w = x >> 1;
         uint32_t lo, hi;
-        if (x & 1) {
-          lo = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-          hi = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-        } else {
-          lo = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-          hi = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
-        }
+        // One byte permute per dword: the (x & 1) halves of rows 0 and 1 (and 2 and 3).
+        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+        lo = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
+        hi = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
         *reinterpret_cast<u32x2*>(s_vt + vt_offset(8 * vc + x, 4 * wave + vs)) = u32x2{lo, hi};
       }
+      // Keep the page-id loads above the barrier (they are used only past it).
+      asm volatile("" ::"s"(next[0]), "s"(next[1]), "s"(next[2]), "s"(next[3]));
       __syncthreads();
-      if (j + 1 < tiles) fetch(j + 1);
+      if (j + 1 < tiles) fetch(j + 1, next);
       if (kTileTok * j > wave_last_pos) continue;   // every row of this wave ends earlier
 
       // S^T for the tile's four 16-token subtiles, both row groups; each K operand is read
@@ -496,13 +505,25 @@ void prefill_kernel(PrefillArgs a, int nx) {
       }
       // O^T += V^T P^T over the tile's two 32-token halves, half-major: consecutive
       // products update different accumulators.
+      // The two 4-token granules of an operand are 32 bytes apart, in either order (the
+      // swizzle swaps them on odd d blocks). Each granule of each half is read through a
+      // base address of its own that the compiler cannot relate to the others, so that
+      // every read lands in its place in the operand rather than in a paired read whose
+      // halves would then be moved.
+      uint32_t vt_base[2][2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t o = static_cast<uint32_t>(vt_offset(col, quad) + 64 * (k >> 1) + 32 * (k & 1));
+        if (k > 0) asm volatile("" : "+v"(o));
+        vt_base[k >> 1][k & 1] = o;
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const int d = 16 * db + col;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + quad));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + vt_offset(d, 8 * c + 4 + quad));
+          const uint32_t off = 16 * db * kVtStride;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(s_vt + vt_base[c][db & 1] + off);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(s_vt + vt_base[c][(db & 1) ^ 1] + off);
           const h8 va = __builtin_bit_cast(h8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           o[0][db] = mfma32(va, pb[0][c], o[0][db]);
           o[1][db] = mfma32(va, pb[1][c], o[1][db]);
