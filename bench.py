@@ -47,7 +47,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published peak
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
 METRIC = "decode-attn KV-read GB/s (fraction of MI355X HBM peak) + µs/step"
 PROFILES = os.path.join(ROOT, "profiles")
-DEFAULT_CONFIG = {"attn": 3, "append": 2, "step": 2, "prefill": 8}
+DEFAULT_CONFIG = {"attn": 3, "append": 2, "step": 2, "prefill": 8, "hbm": 3}
 MIN_WARMUP_S = 0.25   # least GPU work before the timed windows (clocks up after idling)
 
 
@@ -59,10 +59,12 @@ ATTN_SOURCES = ("api.cpp", "kernels.h", "kernels.hip")
 APPEND_SOURCES = ("api.cpp", "kernels.h", "append.hip")
 PREFILL_SOURCES = ("api.cpp", "kernels.h", "prefill.hip")
 STEP_SOURCES = ("api.cpp", "kernels.h", "kernels.hip", "append.hip")
+HBM_SOURCES = ("api.cpp", "kernels.h", "hbm_reference.hip")
 SOURCES_OF_OP = {"attn": ATTN_SOURCES, "append": APPEND_SOURCES, "prefill": PREFILL_SOURCES,
-                 "step": STEP_SOURCES}
+                 "step": STEP_SOURCES, "hbm": HBM_SOURCES}
 PREFIX_OF_OP = {"attn": "decode_attn", "append": "decode_attn_append",
-                "prefill": "decode_attn_prefill", "step": "decode_attn_step"}
+                "prefill": "decode_attn_prefill", "step": "decode_attn_step",
+                "hbm": "hbm_reference"}
 
 
 def strip_comments(text: str) -> str:
@@ -307,10 +309,11 @@ def main():
     ap.add_argument("--kv", choices=["fp16", "bf16", "int8", "fp8"], default=None,
                     help="run the preset's shapes over another storage format (the workload "
                          "name gets the format as a suffix)")
-    ap.add_argument("--op", choices=["attn", "append", "prefill", "step"], default="attn",
+    ap.add_argument("--op", choices=["attn", "append", "prefill", "step", "hbm"], default="attn",
                     help="attn: the decode-attention step (default); append: the K/V append "
                          "that precedes it in a decode step, on the same workload; step: "
-                         "append then attention; prefill: chunked-prefill attention")
+                         "append then attention; prefill: chunked-prefill attention; hbm: "
+                         "reference read rates for the roofline, on the workload's tiles")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="write profiles/<op>_<workload>.txt from the rocprofv3 CSVs in DIR")
     ap.add_argument("--tag", default=None, help="with --summarize-profile: the run's tag")
@@ -351,6 +354,8 @@ def main():
         return bench_prefill(args, cfg, lib, torch, np, binding, generate)
     if args.op == "step":
         return bench_step(args, cfg, lib, torch, np, binding, generate)
+    if args.op == "hbm":
+        return bench_hbm(args, cfg, torch, np, binding)
     log(f"generating {cfg.name} ...")
     w = generate(cfg)
     dev = torch.device("cuda:0")
@@ -451,6 +456,7 @@ def main():
     prof, prof_src = read_profile(cfg.name, "attn")
     traffic = profile_traffic(prof) if prof else None
     log(f"profile: {prof_src}")
+    ref, _ = read_profile(cfg.name, "hbm")
     baseline = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
@@ -510,6 +516,13 @@ def main():
                 "file": prof["_path"],
                 "dominant_kernel_avg_us": round(float(prof["dominant_kernel_timed_avg_ns"]) / 1e3, 3),
                 "traffic_over_algorithmic": float(prof["traffic_over_algorithmic"]),
+            },
+            "attainable": None if not ref else {
+                "what": "best rate of a plain random gather of the same step's 4 KiB K/V "
+                        "tiles (bench.py --op hbm)",
+                "gbs": float(ref["best_gather_gbs"]),
+                "frac": round(achieved / float(ref["best_gather_gbs"]), 4),
+                "file": ref["_path"],
             },
         },
         "hot": hot_rec,
@@ -888,6 +901,85 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
     print(json.dumps(record), flush=True)
 
 
+def bench_hbm(args, cfg, torch, np, binding):
+    """Reference read rates for the HBM roofline (decode_attn_hbm_reference): a random
+    gather of the 4 KiB K and V tiles of one decode step of the workload (every (sequence,
+    KV head, page) tile the step reads, in full, in the order of the sequences and heads),
+    and a plain streaming read of 4 GiB, over several launch shapes. The pools rotate over
+    replicas of at least 1 GiB in all, as in the decode bench, so the Infinity Cache cannot
+    serve them. Prints one JSON line; `best_gather_gbs` is the attainable rate the decode
+    kernels' roofline fraction can be read against."""
+    from decode_phase_attention_paged_amd.workload import layout
+    if cfg.head_dim * cfg.block_size * 2 != 4096:
+        raise SystemExit("the reference gather reads 4 KiB fp16 tiles (head_dim 128, 16-token pages)")
+    lens, table, num_pages = layout(cfg)
+    hkv = cfg.n_kv_heads
+    nb = -(-lens.astype(np.int64) // cfg.block_size)
+    tiles = np.concatenate([table[b, :nb[b]].astype(np.int64) * hkv + g
+                            for b in range(cfg.batch) for g in range(hkv)]).astype(np.int32)
+    count = int(tiles.size)
+    pool_tiles = num_pages * hkv
+    pool_bytes = 2 * pool_tiles * 4096
+    reps = replicas_for(args, pool_bytes)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    k = torch.zeros(reps * pool_tiles * 4096, dtype=torch.uint8, device=dev)
+    v = torch.zeros_like(k)
+    tile_lists = [torch.from_numpy(tiles + r * pool_tiles).to(dev) for r in range(reps)]
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(65535 * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    gather_bytes = 2 * count * 4096
+    results = {"gather": [], "stream": []}
+
+    def measure(kind, depth, nt, grid):
+        if kind == binding.HBM_GATHER:
+            step = lambda i: binding.hbm_reference(kind, k, sink, b=v, tiles=tile_lists[i % reps],
+                                                   depth=depth, nontemporal=nt, grid=grid)
+            nbytes = gather_bytes
+        else:
+            step = lambda i: binding.hbm_reference(kind, buf, sink, depth=depth,
+                                                   nontemporal=nt, grid=grid)
+            nbytes = buf.numel()
+        ms, st = timed_record(args, torch, stream, step, nbytes)
+        row = {"depth": depth, "nontemporal": bool(nt), "grid": grid,
+               "us_per_launch": round(ms * 1e3, 3),
+               "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
+               "gbs_min_max": [round(nbytes / (st["max_ms"] / 1e3) / 1e9, 1),
+                               round(nbytes / (st["min_ms"] / 1e3) / 1e9, 1)]}
+        log(f"{'gather' if kind == binding.HBM_GATHER else 'stream'} {row}")
+        return row
+
+    for nt in (1, 0):
+        for depth in (1, 2, 4):
+            for grid in (256, 512, 1024, 2048):
+                results["gather"].append(measure(binding.HBM_GATHER, depth, nt, grid))
+        for depth in (8, 16):
+            for grid in (512, 1024, 2048):
+                results["stream"].append(measure(binding.HBM_STREAM, depth, nt, grid))
+    if int(sink.abs().sum().item()) != 0:
+        raise RuntimeError("the reference reads folded to their sink key on zero-filled memory")
+    best = {key: max(r["gbs"] for r in rows) for key, rows in results.items()}
+    record = {
+        "metric": "HBM reference read rate (random 4 KiB K/V tile gather; streaming read)",
+        "unit": "GB/s",
+        "best_gather_gbs": best["gather"],
+        "best_stream_gbs": best["stream"],
+        "peak_gbs": HBM_PEAK_GBS,
+        "best_gather_frac_of_peak": round(best["gather"] / HBM_PEAK_GBS, 4),
+        "best_stream_frac_of_peak": round(best["stream"] / HBM_PEAK_GBS, 4),
+        "steps": args.steps,
+        "repeats": args.repeats,
+        "argv": sys.argv[1:],
+        "config": {"workload": cfg.name, "tile_pairs_per_launch": count,
+                   "gather_bytes_per_launch": gather_bytes, "pool_tiles": pool_tiles,
+                   "replicas": reps, "stream_bytes_per_launch": buf.numel()},
+        "gather": results["gather"],
+        "stream": results["stream"],
+    }
+    print(json.dumps(record), flush=True)
+
+
 # ---------------------------------------------------------------------------------------
 # Profile summaries. Layout of DIR for one workload tagged TAG (each a rocprofv3 output
 # directory written with `-d DIR/<name> -o run --output-format csv`, next to the bench.py
@@ -938,11 +1030,61 @@ def _mean(v):
     return sum(v) / len(v) if v else 0.0
 
 
+def summarize_hbm(d: str, tag: str, rec):
+    """profiles/hbm_reference_<workload>.txt: the reference read rates of one
+    `bench.py --op hbm` run under rocprofv3 --kernel-trace --stats, with the trace's
+    average duration of each (kernel, grid) next to the event-timed figures."""
+    argv = [a for a in rec.get("argv", []) if a]
+    workload = rec["config"]["workload"]
+    by = {}
+    for r in _csv_rows(os.path.join(d, f"trace_{tag}", "run_kernel_trace.csv")):
+        name = r["Kernel_Name"]
+        if "ref_gather_kernel" not in name and "ref_stream_kernel" not in name:
+            continue
+        short = name.split("::")[-1].split("(")[0]      # ref_gather_kernel<2, true>
+        key = (short, int(r["Grid_Size_X"]) // 256)
+        by.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    cmd = "python3 $REPO/bench.py " + " ".join(argv)
+    out = [f"# rocprofv3 summary: HBM reference reads, workload {workload}",
+           f"# {json.dumps(rec['config'])}",
+           "# $REPO is the repository root; the command runs from /tmp with TMPDIR=/tmp.",
+           f"# summarised by: python3 $REPO/bench.py --summarize-profile $REPO/gpurun_out/prof --tag {tag}",
+           f"command_trace: rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof/trace_{tag} -o run -- {cmd}",
+           f"kernel_source_sha256: {kernel_source_hash(HBM_SOURCES)}",
+           "",
+           "## kernel trace (per (kernel, grid): every launch of the run, warm-up included)"]
+    for (name, grid), ns in sorted(by.items()):
+        out.append(f"{name} grid {grid}: calls {len(ns)}  avg_ns {_mean(ns):.1f}  "
+                   f"median_ns {statistics.median(ns):.0f}")
+    out += ["", "## event-timed rates (median window; bytes per launch over its time)",
+            f"gather bytes per launch: {rec['config']['gather_bytes_per_launch']} "
+            f"({rec['config']['tile_pairs_per_launch']} K/V tile pairs of 4 KiB)",
+            f"stream bytes per launch: {rec['config']['stream_bytes_per_launch']}"]
+    for kind in ("gather", "stream"):
+        for r in rec[kind]:
+            out.append(f"{kind} depth {r['depth']} nontemporal {int(r['nontemporal'])} grid "
+                       f"{r['grid']}: {r['us_per_launch']} us  {r['gbs']} GB/s  "
+                       f"(windows {r['gbs_min_max'][0]}-{r['gbs_min_max'][1]})")
+    out += ["", "## figures used in the roofline discussion",
+            f"best_gather_gbs: {rec['best_gather_gbs']}",
+            f"best_gather_frac_of_peak: {rec['best_gather_frac_of_peak']}",
+            f"best_stream_gbs: {rec['best_stream_gbs']}",
+            f"best_stream_frac_of_peak: {rec['best_stream_frac_of_peak']}"]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"hbm_reference_{workload}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}: best gather {rec['best_gather_gbs']} GB/s, "
+          f"best stream {rec['best_stream_gbs']} GB/s")
+
+
 def summarize_profile(d: str, tag: str):
     d = os.path.abspath(d)
     trace_dir = os.path.join(d, f"trace_{tag}")
     rec = _last_json(os.path.join(d, f"trace_{tag}.json"))
     argv = [a for a in rec.get("argv", []) if a]
+    if "--op" in argv and argv[argv.index("--op") + 1] == "hbm":
+        return summarize_hbm(d, tag, rec)
     op = "attn"
     if "--op" in argv:
         op = argv[argv.index("--op") + 1]

@@ -90,6 +90,8 @@ _SIGNATURES = {
     "decode_attn_append": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "decode_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                  _I, _I, _F, _P, _P]),
+    "decode_attn_hbm_reference": (_I, [_I, _I, _I, _P, _P, _P, ctypes.c_longlong,
+                                       ctypes.c_longlong, _I, _P, _P]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
 }
@@ -374,3 +376,40 @@ def decode_attn_prefill(q, q_start, k_pages, v_pages, block_table, seq_lens, sca
                                      float(scale), _ptr(out), _stream(dev))
     _check(st, "decode_attn_prefill")
     return out
+
+
+HBM_STREAM = 0
+HBM_GATHER = 1
+
+
+def hbm_reference(kind: int, a: torch.Tensor, sink: torch.Tensor, *, b=None, tiles=None,
+                  depth: int = 2, nontemporal: bool = True, grid: int = 512,
+                  count: Optional[int] = None) -> None:
+    """Reference reads for the HBM roofline (decode_attn_hbm_reference): HBM_STREAM reads
+    ``count`` 16-byte words of ``a`` (default: all of it); HBM_GATHER reads, for every entry
+    t of ``tiles`` (int32), the 4 KiB tile t of ``a`` and of ``b``. ``sink`` is uint32-sized
+    ([grid * 256] int32). Enqueued on torch's current stream of a's device."""
+    lib = load_library()
+    dev = a.device
+    if dev.type != "cuda":
+        raise ValueError("hbm_reference runs on the GPU only")
+    if sink.dtype != torch.int32 or sink.numel() < grid * 256 or sink.device != dev:
+        raise ValueError("sink must be int32 with at least grid * 256 elements on a's device")
+    if kind == HBM_STREAM:
+        words = a.numel() * a.element_size() // 16 if count is None else int(count)
+        st = HBM_STREAM, None, None, words, 0
+    elif kind == HBM_GATHER:
+        if b is None or tiles is None or tiles.dtype != torch.int32:
+            raise ValueError("a gather needs b and int32 tiles")
+        if b.numel() * b.element_size() != a.numel() * a.element_size():
+            raise ValueError("a and b must be pools of the same size")
+        st = HBM_GATHER, b, tiles, tiles.numel() if count is None else int(count), \
+            a.numel() * a.element_size() // 4096
+    else:
+        raise ValueError("kind must be HBM_STREAM or HBM_GATHER")
+    kind, b, tiles, n, num_tiles = st
+    with torch.cuda.device(dev):
+        status = lib.decode_attn_hbm_reference(kind, depth, int(bool(nontemporal)), _ptr(a),
+                                               _ptr(b), _ptr(tiles), n, num_tiles, grid,
+                                               _ptr(sink), _stream(dev))
+    _check(status, "decode_attn_hbm_reference")

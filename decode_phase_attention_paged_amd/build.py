@@ -22,7 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdecode_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["kernels.hip", "append.hip", "prefill.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "append.hip", "prefill.hip", "hbm_reference.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are disabled for all device code.

@@ -17,7 +17,7 @@ namespace {
 using dattn::kBlockSize;
 using dattn::kHeadDim;
 
-constexpr int kVersion = (6 << 16) | 3;
+constexpr int kVersion = (6 << 16) | 4;
 constexpr int kMaxDevices = 64;
 // Stream mode: persistent workgroups per compute unit when the library sizes the grid ...
 constexpr int kStreamWorkgroupsPerCu = 2;
@@ -486,6 +486,35 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
   a.scale_log2 = scale * 1.4426950408889634f;
   if (dattn::launch_prefill(kv_of(kv_dtype), group, a, max_chunk, stream) != hipSuccess)
     return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
+}
+
+int decode_attn_hbm_reference(int kind, int depth, int nontemporal, const void* a,
+                              const void* b, const int32_t* tiles, long long count,
+                              long long num_tiles, int grid, uint32_t* sink,
+                              hipStream_t stream) {
+  if (kind != 0 && kind != 1) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  const bool depth_ok = kind == 0 ? (depth == 4 || depth == 8 || depth == 16)
+                                  : (depth == 1 || depth == 2 || depth == 4);
+  if (!depth_ok || (nontemporal != 0 && nontemporal != 1) || grid < 1 || grid > 65535 ||
+      count < 0 || num_tiles < 0 || a == nullptr || sink == nullptr || !aligned(a, 16))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (kind == 1 && (b == nullptr || tiles == nullptr || !aligned(b, 16) || !aligned(tiles, 4)))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (count == 0) return DECODE_ATTN_OK;
+  (void)hipGetLastError();  // start from a clean error state
+  dattn::HbmReferenceArgs r{};
+  r.kind = kind;
+  r.depth = depth;
+  r.nontemporal = nontemporal;
+  r.grid = grid;
+  r.a = a;
+  r.b = b;
+  r.tiles = tiles;
+  r.count = static_cast<uint64_t>(count);
+  r.num_tiles = static_cast<uint64_t>(num_tiles);
+  r.sink = sink;
+  if (dattn::launch_hbm_reference(r, stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
 

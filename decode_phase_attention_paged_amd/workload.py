@@ -211,21 +211,10 @@ def _finite_e4m3_codes(rng, shape) -> np.ndarray:
     return (u + (u >= 0x7F)).astype(np.uint8)
 
 
-def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False,
-             extra_pages: int = 0, seq_lens: Optional[np.ndarray] = None) -> Workload:
-    """Draw one workload.
-
-    ``seed`` defaults to 1000 + config.index. ``seq_lens`` overrides the drawn
-    lengths (the draw still happens, so the rest of the stream is unchanged).
-    ``extra_pages`` adds pages no sequence references; with ``poison`` those
-    pages and every unused slot of each last page hold NaN (for int8 caches,
-    their row scales do), so any stray read shows up in the output.
-    """
-    c = config
-    seed = 1000 + c.index if seed is None else int(seed)
-    rng = np.random.default_rng(seed)
-    bs, hkv, d = c.block_size, c.n_kv_heads, c.head_dim
-
+def _draw_layout(c: Config, rng, seq_lens=None, extra_pages: int = 0):
+    """The first draws of a workload: lengths, then the page permutation behind the block
+    table. Returns (seq_lens, block_table, pages in use, pages in the pool)."""
+    bs = c.block_size
     lens = rng.integers(c.len_lo, c.len_hi + 1, size=c.batch).astype(np.int32)
     if seq_lens is not None:
         lens = np.asarray(seq_lens, dtype=np.int32).copy()
@@ -245,6 +234,32 @@ def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False
         nb = int(n_blocks[b])
         table[b, :nb] = perm[offset:offset + nb]
         offset += nb
+    return lens, table, n_used, n_pages
+
+
+def layout(config: Config, seed: Optional[int] = None):
+    """(seq_lens, block_table, num_pages) of the workload generate(config, seed) draws,
+    without drawing its tensors."""
+    seed = 1000 + config.index if seed is None else int(seed)
+    lens, table, _, n_pages = _draw_layout(config, np.random.default_rng(seed))
+    return lens, table, n_pages
+
+
+def generate(config: Config, seed: Optional[int] = None, *, poison: bool = False,
+             extra_pages: int = 0, seq_lens: Optional[np.ndarray] = None) -> Workload:
+    """Draw one workload.
+
+    ``seed`` defaults to 1000 + config.index. ``seq_lens`` overrides the drawn
+    lengths (the draw still happens, so the rest of the stream is unchanged).
+    ``extra_pages`` adds pages no sequence references; with ``poison`` those
+    pages and every unused slot of each last page hold NaN (for int8 caches,
+    their row scales do), so any stray read shows up in the output.
+    """
+    c = config
+    seed = 1000 + c.index if seed is None else int(seed)
+    rng = np.random.default_rng(seed)
+    bs, hkv, d = c.block_size, c.n_kv_heads, c.head_dim
+    lens, table, n_used, n_pages = _draw_layout(c, rng, seq_lens, extra_pages)
 
     q = rng.standard_normal((c.batch, c.n_q_heads, d), dtype=np.float32)
     q = _bf16_bits(q) if c.kv_dtype == "bf16" else q.astype(np.float16)

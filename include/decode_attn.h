@@ -307,12 +307,44 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
                         int n_kv_heads, int head_dim, int block_size, int kv_dtype, int max_chunk,
                         float scale, float* out, hipStream_t stream);
 
+/*
+ * Reference reads for the HBM roofline; a measurement aid, not part of the attention path.
+ * Decode attention streams the KV cache once per step and is bound by HBM bandwidth (xLLM
+ * README, bottleneck analysis: attention score and output are memory-bound), so its
+ * kernels are judged against the rate at which this GPU can read the same bytes. These
+ * kernels read memory the way the decode kernels do, 16 bytes per lane, and fold the bits
+ * into one value without other arithmetic:
+ *
+ *     kind 0  streaming read of `count` 16-byte words at `a` (b and tiles unused);
+ *             depth = words per lane per step: 4, 8 or 16
+ *     kind 1  tile gather: for every i < count, the 4 KiB tile tiles[i] of `a` and the
+ *             one of `b` (tile t at byte offset 4096 t), as the decode kernels read the
+ *             fp16 K and V tiles of one (page, KV head); entries outside [0, num_tiles)
+ *             are skipped. Each wave takes an equal contiguous run of entries; depth =
+ *             entries in flight per wave: 1, 2 or 4
+ *
+ *     nontemporal  1: loads carry the non-temporal hint (as the decode kernels'), 0: not
+ *     grid         workgroups of 256 threads, 1 .. 65535
+ *     sink         device uint32 [grid * 256]; a lane writes its fold there only if it
+ *                  equals one fixed 32-bit value (never, for zero-filled memory)
+ *
+ * a, b and tiles are device pointers: a and b 16-byte aligned, tiles 4-byte aligned, a at
+ * least 16 count bytes (kind 0), a and b at least 4096 num_tiles bytes (kind 1). Nothing is
+ * written but the sink. Asynchronous on `stream`; never allocates. Returns
+ * DECODE_ATTN_ERR_INVALID_ARGUMENT for any other kind, depth, nontemporal or grid, a null
+ * or misaligned pointer, or a negative count or num_tiles.
+ */
+int decode_attn_hbm_reference(int kind, int depth, int nontemporal, const void* a,
+                              const void* b, const int32_t* tiles, long long count,
+                              long long num_tiles, int grid, uint32_t* sink,
+                              hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);
 
 /* Library ABI version: (major << 16) | minor. 6.0 adds the BF16 and FP8 formats;
    6.1 adds decode_attn_prefill; 6.2 gives it every storage format (row scale arguments);
-   6.3 adds decode_attn_noalloc. */
+   6.3 adds decode_attn_noalloc; 6.4 adds decode_attn_hbm_reference. */
 int decode_attn_version(void);
 
 #ifdef __cplusplus

@@ -34,9 +34,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_noalloc",
-        "decode_attn_plan", "decode_attn_prefill", "decode_attn_status_string",
-        "decode_attn_version"])
+        "decode_attn", "decode_attn_append", "decode_attn_ex", "decode_attn_hbm_reference",
+        "decode_attn_noalloc", "decode_attn_plan", "decode_attn_prefill",
+        "decode_attn_status_string", "decode_attn_version"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -52,7 +52,7 @@ def test_plan_struct_matches_the_header(binding):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 3
+    assert lib.decode_attn_version() >> 16 == 6 and lib.decode_attn_version() & 0xFFFF >= 4
     names = [lib.decode_attn_status_string(i).decode() for i in range(6)]
     assert names == ["DECODE_ATTN_OK", "DECODE_ATTN_ERR_INVALID_ARGUMENT",
                      "DECODE_ATTN_ERR_UNSUPPORTED", "DECODE_ATTN_ERR_WORKSPACE",
@@ -358,3 +358,28 @@ def call_prefill(lib, **over):
 ])
 def test_prefill_host_validation(lib, over, status):
     assert call_prefill(lib, **over) == status
+
+
+def call_hbm(lib, **over):
+    a = dict(kind=1, depth=2, nt=1, a=A, b=2 * A, tiles=3 * A, count=100, num_tiles=64,
+             grid=8, sink=4 * A)
+    a.update(over)
+    return lib.decode_attn_hbm_reference(a["kind"], a["depth"], a["nt"], a["a"], a["b"],
+                                         a["tiles"], a["count"], a["num_tiles"], a["grid"],
+                                         a["sink"], None)
+
+
+@pytest.mark.parametrize("over", [
+    dict(kind=2), dict(kind=-1), dict(depth=3), dict(depth=8), dict(kind=0, depth=2),
+    dict(kind=0, depth=1), dict(nt=2), dict(grid=0), dict(grid=65536), dict(count=-1),
+    dict(num_tiles=-1), dict(a=None), dict(sink=None), dict(a=A + 4), dict(b=None),
+    dict(tiles=None), dict(b=2 * A + 8), dict(tiles=3 * A + 2),
+])
+def test_hbm_reference_rejects_bad_arguments(lib, over):
+    assert call_hbm(lib, **over) == 1     # DECODE_ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_hbm_reference_empty_enqueues_nothing(lib):
+    # count 0 returns before any HIP call; a streaming read needs neither b nor tiles
+    assert call_hbm(lib, count=0) == 0
+    assert call_hbm(lib, kind=0, depth=8, b=None, tiles=None, count=0) == 0

@@ -154,3 +154,42 @@ def test_build_reads_scratch_from_resource_remarks():
     ])
     assert build.scratch_use(remarks) == {"_Z3fooPf": 0, "_Z3barPf": 24}
     assert build.scratch_use("no remarks here") == {}
+
+
+def test_summarize_hbm_reference_on_synthetic_output(tmp_path, monkeypatch):
+    """A fake `bench.py --op hbm` run under the kernel trace: the summary groups launches
+    by (kernel, grid), copies the event-timed rates and the best ones, and names the
+    command and the source hash of the reference kernels."""
+    d = tmp_path / "prof"
+    d.mkdir()
+    tag = "hbm"
+    rec = {"metric": "HBM reference read rate", "argv": ["--op", "hbm", "--steps", "10"],
+           "best_gather_gbs": 6700.0, "best_stream_gbs": 7100.0,
+           "best_gather_frac_of_peak": 0.8375, "best_stream_frac_of_peak": 0.8875,
+           "config": {"workload": "synthetic_case", "gather_bytes_per_launch": 8192,
+                      "tile_pairs_per_launch": 1, "stream_bytes_per_launch": 4096},
+           "gather": [{"depth": 2, "nontemporal": True, "grid": 512, "us_per_launch": 1.0,
+                       "gbs": 6700.0, "gbs_min_max": [6600.0, 6750.0]}],
+           "stream": [{"depth": 8, "nontemporal": False, "grid": 1024, "us_per_launch": 2.0,
+                       "gbs": 7100.0, "gbs_min_max": [7000.0, 7150.0]}]}
+    (d / f"trace_{tag}.json").write_text("progress\n" + json.dumps(rec) + "\n")
+    gk = "void dattn::(anonymous namespace)::ref_gather_kernel<2, true>(...)"
+    sk = "void dattn::(anonymous namespace)::ref_stream_kernel<8, false>(...)"
+    rows = [{"Kernel_Name": gk, "Start_Timestamp": 0, "End_Timestamp": 1000, "Grid_Size_X": 512 * 256},
+            {"Kernel_Name": gk, "Start_Timestamp": 0, "End_Timestamp": 3000, "Grid_Size_X": 512 * 256},
+            {"Kernel_Name": gk, "Start_Timestamp": 0, "End_Timestamp": 5000, "Grid_Size_X": 256 * 256},
+            {"Kernel_Name": sk, "Start_Timestamp": 0, "End_Timestamp": 2000, "Grid_Size_X": 1024 * 256},
+            {"Kernel_Name": "__amd_rocclr_fillBufferAligned", "Start_Timestamp": 0,
+             "End_Timestamp": 9, "Grid_Size_X": 64}]
+    _write_csv(str(d / f"trace_{tag}" / "run_kernel_trace.csv"), rows)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    bench.summarize_profile(str(d), tag)
+    text = (tmp_path / "hbm_reference_synthetic_case.txt").read_text()
+    assert "ref_gather_kernel<2, true> grid 512: calls 2  avg_ns 2000.0" in text
+    assert "ref_gather_kernel<2, true> grid 256: calls 1  avg_ns 5000.0" in text
+    assert "ref_stream_kernel<8, false> grid 1024: calls 1  avg_ns 2000.0" in text
+    assert "rocclr" not in text
+    assert "gather depth 2 nontemporal 1 grid 512: 1.0 us  6700.0 GB/s  (windows 6600.0-6750.0)" in text
+    assert "best_stream_gbs: 7100.0" in text
+    assert "-- python3 $REPO/bench.py --op hbm --steps 10" in text
+    assert f"kernel_source_sha256: {bench.kernel_source_hash(bench.HBM_SOURCES)}" in text
