@@ -308,8 +308,9 @@ struct Tile {
 };
 
 // Cache tiles are read once per step, so their loads carry the non-temporal hint: a random
-// 4 KiB tile gather streams about 13 % faster from HBM with it than without (6.7-6.9 against
-// 5.9-6.0 TB/s on MI355X), and a plain streaming read 7.0-7.2 against 6.2-6.4 TB/s.
+// 4 KiB tile gather streams about 12 % faster from HBM with it than without (6.6-6.7 against
+// 5.9-6.0 TB/s on MI355X, measured with the reference reads of hbm_reference.hip), and a
+// plain streaming read 6.7-7.1 against 5.8-6.3 TB/s.
 template <typename T>
 __device__ __forceinline__ T stream_load(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
