@@ -518,8 +518,8 @@ def main():
                 "traffic_over_algorithmic": float(prof["traffic_over_algorithmic"]),
             },
             "attainable": None if not ref else {
-                "what": "best rate of a plain random gather of the same step's 4 KiB K/V "
-                        "tiles (bench.py --op hbm)",
+                "what": "best rate of a plain random gather of the same step's K/V tiles "
+                        "(bench.py --op hbm)",
                 "gbs": float(ref["best_gather_gbs"]),
                 "frac": round(achieved / float(ref["best_gather_gbs"]), 4),
                 "file": ref["_path"],
@@ -903,15 +903,19 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
 
 def bench_hbm(args, cfg, torch, np, binding):
     """Reference read rates for the HBM roofline (decode_attn_hbm_reference): a random
-    gather of the 4 KiB K and V tiles of one decode step of the workload (every (sequence,
-    KV head, page) tile the step reads, in full, in the order of the sequences and heads),
-    and a plain streaming read of 4 GiB, over several launch shapes. The pools rotate over
-    replicas of at least 1 GiB in all, as in the decode bench, so the Infinity Cache cannot
-    serve them. Prints one JSON line; `best_gather_gbs` is the attainable rate the decode
-    kernels' roofline fraction can be read against."""
+    gather of the K and V tiles of one decode step of the workload (every (sequence, KV
+    head, page) tile the step reads, in full, in the order of the sequences and heads:
+    4 KiB tiles for 16-bit formats, 2 KiB of codes plus the 64-byte row-scale records for
+    INT8 and FP8), and a plain streaming read of 4 GiB, over several launch shapes. The
+    pools rotate over replicas of at least 1 GiB in all, as in the decode bench, so the
+    Infinity Cache cannot serve them. Prints one JSON line; `best_gather_gbs` is the
+    attainable rate the decode kernels' roofline fraction can be read against."""
     from decode_phase_attention_paged_amd.workload import layout
-    if cfg.head_dim * cfg.block_size * 2 != 4096:
-        raise SystemExit("the reference gather reads 4 KiB fp16 tiles (head_dim 128, 16-token pages)")
+    elem = 2 if cfg.kv_dtype in ("fp16", "bf16") else 1
+    tile_bytes = cfg.head_dim * cfg.block_size * elem
+    if cfg.head_dim != 128 or cfg.block_size != 16:
+        raise SystemExit("the reference gather reads the tiles of head_dim 128, 16-token pages")
+    kind = binding.HBM_GATHER if elem == 2 else binding.HBM_GATHER_SCALED
     lens, table, num_pages = layout(cfg)
     hkv = cfg.n_kv_heads
     nb = -(-lens.astype(np.int64) // cfg.block_size)
@@ -919,23 +923,29 @@ def bench_hbm(args, cfg, torch, np, binding):
                             for b in range(cfg.batch) for g in range(hkv)]).astype(np.int32)
     count = int(tiles.size)
     pool_tiles = num_pages * hkv
-    pool_bytes = 2 * pool_tiles * 4096
+    record = 64 if elem == 1 else 0
+    pool_bytes = 2 * pool_tiles * (tile_bytes + record)
     reps = replicas_for(args, pool_bytes)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    k = torch.zeros(reps * pool_tiles * 4096, dtype=torch.uint8, device=dev)
+    k = torch.zeros(reps * pool_tiles * tile_bytes, dtype=torch.uint8, device=dev)
     v = torch.zeros_like(k)
+    ks = vs = None
+    if record:
+        ks = torch.zeros(reps * pool_tiles * record, dtype=torch.uint8, device=dev)
+        vs = torch.zeros_like(ks)
     tile_lists = [torch.from_numpy(tiles + r * pool_tiles).to(dev) for r in range(reps)]
     buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(65535 * 256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    gather_bytes = 2 * count * 4096
+    gather_bytes = 2 * count * (tile_bytes + record)
     results = {"gather": [], "stream": []}
 
     def measure(kind, depth, nt, grid):
-        if kind == binding.HBM_GATHER:
+        if kind != binding.HBM_STREAM:
             step = lambda i: binding.hbm_reference(kind, k, sink, b=v, tiles=tile_lists[i % reps],
-                                                   depth=depth, nontemporal=nt, grid=grid)
+                                                   a_scale=ks, b_scale=vs, depth=depth,
+                                                   nontemporal=nt, grid=grid)
             nbytes = gather_bytes
         else:
             step = lambda i: binding.hbm_reference(kind, buf, sink, depth=depth,
@@ -947,13 +957,13 @@ def bench_hbm(args, cfg, torch, np, binding):
                "gbs": round(nbytes / (ms / 1e3) / 1e9, 1),
                "gbs_min_max": [round(nbytes / (st["max_ms"] / 1e3) / 1e9, 1),
                                round(nbytes / (st["min_ms"] / 1e3) / 1e9, 1)]}
-        log(f"{'gather' if kind == binding.HBM_GATHER else 'stream'} {row}")
+        log(f"{'stream' if kind == binding.HBM_STREAM else 'gather'} {row}")
         return row
 
     for nt in (1, 0):
         for depth in (1, 2, 4):
             for grid in (256, 512, 1024, 2048):
-                results["gather"].append(measure(binding.HBM_GATHER, depth, nt, grid))
+                results["gather"].append(measure(kind, depth, nt, grid))
         for depth in (8, 16):
             for grid in (512, 1024, 2048):
                 results["stream"].append(measure(binding.HBM_STREAM, depth, nt, grid))
@@ -961,7 +971,7 @@ def bench_hbm(args, cfg, torch, np, binding):
         raise RuntimeError("the reference reads folded to their sink key on zero-filled memory")
     best = {key: max(r["gbs"] for r in rows) for key, rows in results.items()}
     record = {
-        "metric": "HBM reference read rate (random 4 KiB K/V tile gather; streaming read)",
+        "metric": "HBM reference read rate (random K/V tile gather; streaming read)",
         "unit": "GB/s",
         "best_gather_gbs": best["gather"],
         "best_stream_gbs": best["stream"],
@@ -971,7 +981,8 @@ def bench_hbm(args, cfg, torch, np, binding):
         "steps": args.steps,
         "repeats": args.repeats,
         "argv": sys.argv[1:],
-        "config": {"workload": cfg.name, "tile_pairs_per_launch": count,
+        "config": {"workload": cfg.name, "kv_dtype": cfg.kv_dtype, "tile_bytes": tile_bytes,
+                   "scale_record_bytes": record, "tile_pairs_per_launch": count,
                    "gather_bytes_per_launch": gather_bytes, "pool_tiles": pool_tiles,
                    "replicas": reps, "stream_bytes_per_launch": buf.numel()},
         "gather": results["gather"],
@@ -1058,7 +1069,10 @@ def summarize_hbm(d: str, tag: str, rec):
                    f"median_ns {statistics.median(ns):.0f}")
     out += ["", "## event-timed rates (median window; bytes per launch over its time)",
             f"gather bytes per launch: {rec['config']['gather_bytes_per_launch']} "
-            f"({rec['config']['tile_pairs_per_launch']} K/V tile pairs of 4 KiB)",
+            f"({rec['config']['tile_pairs_per_launch']} K/V tile pairs of "
+            f"{rec['config'].get('tile_bytes', 4096)} bytes"
+            + (f" and their {rec['config']['scale_record_bytes']}-byte scale records)"
+               if rec['config'].get('scale_record_bytes') else ")"),
             f"stream bytes per launch: {rec['config']['stream_bytes_per_launch']}"]
     for kind in ("gather", "stream"):
         for r in rec[kind]:

@@ -90,7 +90,7 @@ _SIGNATURES = {
     "decode_attn_append": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "decode_attn_prefill": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                  _I, _I, _F, _P, _P]),
-    "decode_attn_hbm_reference": (_I, [_I, _I, _I, _P, _P, _P, ctypes.c_longlong,
+    "decode_attn_hbm_reference": (_I, [_I, _I, _I, _P, _P, _P, _P, _P, ctypes.c_longlong,
                                        ctypes.c_longlong, _I, _P, _P]),
     "decode_attn_status_string": (ctypes.c_char_p, [_I]),
     "decode_attn_version": (_I, []),
@@ -379,37 +379,49 @@ def decode_attn_prefill(q, q_start, k_pages, v_pages, block_table, seq_lens, sca
 
 
 HBM_STREAM = 0
-HBM_GATHER = 1
+HBM_GATHER = 1          # 4 KiB tiles (16-bit K/V)
+HBM_GATHER_SCALED = 2   # 2 KiB tiles plus 64-byte row-scale records (1-byte K/V)
+_HBM_TILE_BYTES = {HBM_GATHER: 4096, HBM_GATHER_SCALED: 2048}
 
 
 def hbm_reference(kind: int, a: torch.Tensor, sink: torch.Tensor, *, b=None, tiles=None,
-                  depth: int = 2, nontemporal: bool = True, grid: int = 512,
-                  count: Optional[int] = None) -> None:
+                  a_scale=None, b_scale=None, depth: int = 2, nontemporal: bool = True,
+                  grid: int = 512, count: Optional[int] = None) -> None:
     """Reference reads for the HBM roofline (decode_attn_hbm_reference): HBM_STREAM reads
     ``count`` 16-byte words of ``a`` (default: all of it); HBM_GATHER reads, for every entry
-    t of ``tiles`` (int32), the 4 KiB tile t of ``a`` and of ``b``. ``sink`` is uint32-sized
-    ([grid * 256] int32). Enqueued on torch's current stream of a's device."""
+    t of ``tiles`` (int32), the 4 KiB tile t of ``a`` and of ``b``; HBM_GATHER_SCALED the
+    2 KiB tile t of each and the 64-byte records t of ``a_scale`` and ``b_scale``. ``sink``
+    is int32 [>= grid * 256]. Enqueued on torch's current stream of a's device."""
     lib = load_library()
     dev = a.device
     if dev.type != "cuda":
         raise ValueError("hbm_reference runs on the GPU only")
     if sink.dtype != torch.int32 or sink.numel() < grid * 256 or sink.device != dev:
         raise ValueError("sink must be int32 with at least grid * 256 elements on a's device")
+    nbytes = lambda t: t.numel() * t.element_size()
     if kind == HBM_STREAM:
-        words = a.numel() * a.element_size() // 16 if count is None else int(count)
-        st = HBM_STREAM, None, None, words, 0
-    elif kind == HBM_GATHER:
+        n = nbytes(a) // 16 if count is None else int(count)
+        b = tiles = a_scale = b_scale = None
+        num_tiles = 0
+    elif kind in _HBM_TILE_BYTES:
         if b is None or tiles is None or tiles.dtype != torch.int32:
             raise ValueError("a gather needs b and int32 tiles")
-        if b.numel() * b.element_size() != a.numel() * a.element_size():
+        if nbytes(b) != nbytes(a):
             raise ValueError("a and b must be pools of the same size")
-        st = HBM_GATHER, b, tiles, tiles.numel() if count is None else int(count), \
-            a.numel() * a.element_size() // 4096
+        num_tiles = nbytes(a) // _HBM_TILE_BYTES[kind]
+        if kind == HBM_GATHER_SCALED:
+            if a_scale is None or b_scale is None:
+                raise ValueError("a scaled gather needs a_scale and b_scale")
+            if min(nbytes(a_scale), nbytes(b_scale)) < 64 * num_tiles:
+                raise ValueError("a_scale and b_scale need 64 bytes per tile")
+        else:
+            a_scale = b_scale = None
+        n = tiles.numel() if count is None else int(count)
     else:
-        raise ValueError("kind must be HBM_STREAM or HBM_GATHER")
-    kind, b, tiles, n, num_tiles = st
+        raise ValueError("kind must be HBM_STREAM, HBM_GATHER or HBM_GATHER_SCALED")
     with torch.cuda.device(dev):
         status = lib.decode_attn_hbm_reference(kind, depth, int(bool(nontemporal)), _ptr(a),
-                                               _ptr(b), _ptr(tiles), n, num_tiles, grid,
-                                               _ptr(sink), _stream(dev))
+                                               _ptr(b), _ptr(a_scale), _ptr(b_scale),
+                                               _ptr(tiles), n, num_tiles, grid, _ptr(sink),
+                                               _stream(dev))
     _check(status, "decode_attn_hbm_reference")

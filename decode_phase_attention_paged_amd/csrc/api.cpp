@@ -490,16 +490,19 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
 }
 
 int decode_attn_hbm_reference(int kind, int depth, int nontemporal, const void* a,
-                              const void* b, const int32_t* tiles, long long count,
-                              long long num_tiles, int grid, uint32_t* sink,
-                              hipStream_t stream) {
-  if (kind != 0 && kind != 1) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+                              const void* b, const void* a_scale, const void* b_scale,
+                              const int32_t* tiles, long long count, long long num_tiles,
+                              int grid, uint32_t* sink, hipStream_t stream) {
+  if (kind < 0 || kind > 2) return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   const bool depth_ok = kind == 0 ? (depth == 4 || depth == 8 || depth == 16)
                                   : (depth == 1 || depth == 2 || depth == 4);
   if (!depth_ok || (nontemporal != 0 && nontemporal != 1) || grid < 1 || grid > 65535 ||
       count < 0 || num_tiles < 0 || a == nullptr || sink == nullptr || !aligned(a, 16))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
-  if (kind == 1 && (b == nullptr || tiles == nullptr || !aligned(b, 16) || !aligned(tiles, 4)))
+  if (kind >= 1 && (b == nullptr || tiles == nullptr || !aligned(b, 16) || !aligned(tiles, 4)))
+    return DECODE_ATTN_ERR_INVALID_ARGUMENT;
+  if (kind == 2 && (a_scale == nullptr || b_scale == nullptr || !aligned(a_scale, 64) ||
+                    !aligned(b_scale, 64)))
     return DECODE_ATTN_ERR_INVALID_ARGUMENT;
   if (count == 0) return DECODE_ATTN_OK;
   (void)hipGetLastError();  // start from a clean error state
@@ -510,6 +513,8 @@ int decode_attn_hbm_reference(int kind, int depth, int nontemporal, const void* 
   r.grid = grid;
   r.a = a;
   r.b = b;
+  r.a_scale = a_scale;
+  r.b_scale = b_scale;
   r.tiles = tiles;
   r.count = static_cast<uint64_t>(count);
   r.num_tiles = static_cast<uint64_t>(num_tiles);

@@ -144,16 +144,20 @@ hipError_t launch_prefill(KvType kv, int group, const PrefillArgs& a, int max_ch
 
 // Reference reads for the HBM roofline (hbm_reference.hip); the host has checked every field.
 struct HbmReferenceArgs {
-  int kind;                    // 0: streaming read of a, 1: tile gather from a and b
+  int kind;                    // 0: streaming read of a; 1: 4 KiB tile gather from a and
+                               // b; 2: 2 KiB tile gather from a and b with 64-byte scale
+                               // records from a_scale and b_scale
   int depth;                   // kind 0: 16-byte words per lane per step (4, 8, 16);
-                               // kind 1: tile pairs in flight per wave (1, 2, 4)
+                               // kinds 1, 2: tile pairs in flight per wave (1, 2, 4)
   int nontemporal;             // 1: loads carry the non-temporal hint, as the decode kernels'
   int grid;                    // workgroups of 256 threads
   const void* a;
   const void* b;
-  const int32_t* tiles;        // kind 1: tile indices
-  uint64_t count;              // kind 0: 16-byte words; kind 1: entries of tiles
-  uint64_t num_tiles;          // kind 1: 4 KiB tiles in each of a and b
+  const void* a_scale;         // kind 2
+  const void* b_scale;
+  const int32_t* tiles;        // kinds 1, 2: tile indices
+  uint64_t count;              // kind 0: 16-byte words; kinds 1, 2: entries of tiles
+  uint64_t num_tiles;          // kinds 1, 2: tiles in each of a and b
   uint32_t* sink;              // uint32 [grid * 256]
 };
 hipError_t launch_hbm_reference(const HbmReferenceArgs& r, hipStream_t stream);

@@ -315,29 +315,35 @@ int decode_attn_prefill(const void* q, const int32_t* q_start, const void* k_pag
  * kernels read memory the way the decode kernels do, 16 bytes per lane, and fold the bits
  * into one value without other arithmetic:
  *
- *     kind 0  streaming read of `count` 16-byte words at `a` (b and tiles unused);
+ *     kind 0  streaming read of `count` 16-byte words at `a` (nothing else used);
  *             depth = words per lane per step: 4, 8 or 16
  *     kind 1  tile gather: for every i < count, the 4 KiB tile tiles[i] of `a` and the
  *             one of `b` (tile t at byte offset 4096 t), as the decode kernels read the
- *             fp16 K and V tiles of one (page, KV head); entries outside [0, num_tiles)
- *             are skipped. Each wave takes an equal contiguous run of entries; depth =
- *             entries in flight per wave: 1, 2 or 4
+ *             16-bit K and V tiles of one (page, KV head)
+ *     kind 2  as kind 1 with 2 KiB tiles (offset 2048 t), plus the 64-byte records
+ *             a_scale + 64 t and b_scale + 64 t: the codes and row scales of a 1-byte
+ *             (INT8 or FP8) tile
  *
+ *     For kinds 1 and 2, entries of tiles outside [0, num_tiles) are skipped; each wave
+ *     takes an equal contiguous run of entries, and depth = entries in flight per wave:
+ *     1, 2 or 4.
  *     nontemporal  1: loads carry the non-temporal hint (as the decode kernels'), 0: not
  *     grid         workgroups of 256 threads, 1 .. 65535
  *     sink         device uint32 [grid * 256]; a lane writes its fold there only if it
  *                  equals one fixed 32-bit value (never, for zero-filled memory)
  *
- * a, b and tiles are device pointers: a and b 16-byte aligned, tiles 4-byte aligned, a at
- * least 16 count bytes (kind 0), a and b at least 4096 num_tiles bytes (kind 1). Nothing is
- * written but the sink. Asynchronous on `stream`; never allocates. Returns
- * DECODE_ATTN_ERR_INVALID_ARGUMENT for any other kind, depth, nontemporal or grid, a null
- * or misaligned pointer, or a negative count or num_tiles.
+ * All pointers are device pointers: a and b 16-byte aligned, a_scale and b_scale 64-byte
+ * aligned (kind 2 only; ignored otherwise), tiles 4-byte aligned. `a` holds at least
+ * 16 count bytes (kind 0); a and b hold num_tiles tiles, a_scale and b_scale num_tiles
+ * records (kinds 1, 2). Nothing is written but the sink. Asynchronous on `stream`; never
+ * allocates. Returns DECODE_ATTN_ERR_INVALID_ARGUMENT for any other kind, depth,
+ * nontemporal or grid, a null or misaligned pointer that the kind uses, or a negative
+ * count or num_tiles.
  */
 int decode_attn_hbm_reference(int kind, int depth, int nontemporal, const void* a,
-                              const void* b, const int32_t* tiles, long long count,
-                              long long num_tiles, int grid, uint32_t* sink,
-                              hipStream_t stream);
+                              const void* b, const void* a_scale, const void* b_scale,
+                              const int32_t* tiles, long long count, long long num_tiles,
+                              int grid, uint32_t* sink, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_string(int status);

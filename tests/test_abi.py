@@ -361,19 +361,21 @@ def test_prefill_host_validation(lib, over, status):
 
 
 def call_hbm(lib, **over):
-    a = dict(kind=1, depth=2, nt=1, a=A, b=2 * A, tiles=3 * A, count=100, num_tiles=64,
-             grid=8, sink=4 * A)
+    a = dict(kind=1, depth=2, nt=1, a=A, b=2 * A, asc=5 * A, bsc=6 * A, tiles=3 * A,
+             count=100, num_tiles=64, grid=8, sink=4 * A)
     a.update(over)
     return lib.decode_attn_hbm_reference(a["kind"], a["depth"], a["nt"], a["a"], a["b"],
-                                         a["tiles"], a["count"], a["num_tiles"], a["grid"],
-                                         a["sink"], None)
+                                         a["asc"], a["bsc"], a["tiles"], a["count"],
+                                         a["num_tiles"], a["grid"], a["sink"], None)
 
 
 @pytest.mark.parametrize("over", [
-    dict(kind=2), dict(kind=-1), dict(depth=3), dict(depth=8), dict(kind=0, depth=2),
-    dict(kind=0, depth=1), dict(nt=2), dict(grid=0), dict(grid=65536), dict(count=-1),
-    dict(num_tiles=-1), dict(a=None), dict(sink=None), dict(a=A + 4), dict(b=None),
-    dict(tiles=None), dict(b=2 * A + 8), dict(tiles=3 * A + 2),
+    dict(kind=3), dict(kind=-1), dict(depth=3), dict(depth=8), dict(kind=0, depth=2),
+    dict(kind=0, depth=1), dict(kind=2, depth=16), dict(nt=2), dict(grid=0),
+    dict(grid=65536), dict(count=-1), dict(num_tiles=-1), dict(a=None), dict(sink=None),
+    dict(a=A + 4), dict(b=None), dict(tiles=None), dict(b=2 * A + 8), dict(tiles=3 * A + 2),
+    dict(kind=2, asc=None), dict(kind=2, bsc=None), dict(kind=2, asc=5 * A + 32),
+    dict(kind=2, bsc=6 * A + 16),
 ])
 def test_hbm_reference_rejects_bad_arguments(lib, over):
     assert call_hbm(lib, **over) == 1     # DECODE_ATTN_ERR_INVALID_ARGUMENT
@@ -382,4 +384,7 @@ def test_hbm_reference_rejects_bad_arguments(lib, over):
 def test_hbm_reference_empty_enqueues_nothing(lib):
     # count 0 returns before any HIP call; a streaming read needs neither b nor tiles
     assert call_hbm(lib, count=0) == 0
-    assert call_hbm(lib, kind=0, depth=8, b=None, tiles=None, count=0) == 0
+    assert call_hbm(lib, kind=2, count=0) == 0
+    # a streaming read needs neither b, tiles nor scales; a 4 KiB gather no scales
+    assert call_hbm(lib, kind=0, depth=8, b=None, tiles=None, asc=None, bsc=None, count=0) == 0
+    assert call_hbm(lib, kind=1, asc=None, bsc=None, count=0) == 0

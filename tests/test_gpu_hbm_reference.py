@@ -1,8 +1,8 @@
 """The HBM reference reads (decode_attn_hbm_reference) through the C ABI: they read the
-words and tiles they are given and nothing else, skip tile entries outside the pool, and
-write only their sink. Each case plants one 32-bit word so that exactly one lane's fold
-of what it read equals the sink key; that lane, and no other, must write the key. Their
-rates are measured by `bench.py --op hbm`, not here."""
+words, tiles and scale records they are given and nothing else, skip tile entries outside
+the pool, and write only their sink. Each case plants one 32-bit word so that exactly the
+lanes whose fold of what they read equals the sink key write it. Their rates are measured
+by `bench.py --op hbm`, not here."""
 
 import pytest
 
@@ -70,6 +70,28 @@ def test_gather_reads_the_listed_tiles_only(torch, binding, depth, nt):
                           nontemporal=nt, grid=1)
     # One entry over four waves: the last wave takes it.
     assert hits(torch, sink) == ([3 * 64 + lane], [KEY_I32])
+
+
+@pytest.mark.parametrize("depth", [1, 2, 4])
+@pytest.mark.parametrize("nt", [True, False])
+def test_scaled_gather_reads_codes_and_scale_records(torch, binding, depth, nt):
+    n_tiles, t = 29, 11
+    tiles = torch.tensor([t, -5, n_tiles, 2 * n_tiles], dtype=torch.int32, device="cuda:0")
+    zeros = lambda n: torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+    # The key in V's 2 KiB tile t, at the word lane 40 reads with its second load.
+    v = plant(torch, n_tiles * 2048, t * 2048 + 1024 + 40 * 16)
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    binding.hbm_reference(binding.HBM_GATHER_SCALED, zeros(n_tiles * 2048), sink, b=v,
+                          tiles=tiles, a_scale=zeros(n_tiles * 64), b_scale=zeros(n_tiles * 64),
+                          depth=depth, nontemporal=nt, grid=1)
+    assert hits(torch, sink) == ([40], [KEY_I32])          # entry 0 is wave 0's
+    # The key in dword 7 of K's scale record t: lanes 7, 23, 39 and 55 each read it once.
+    ks = plant(torch, n_tiles * 64, t * 64 + 7 * 4)
+    sink.zero_()
+    binding.hbm_reference(binding.HBM_GATHER_SCALED, zeros(n_tiles * 2048), sink,
+                          b=zeros(n_tiles * 2048), tiles=tiles, a_scale=ks,
+                          b_scale=zeros(n_tiles * 64), depth=depth, nontemporal=nt, grid=1)
+    assert hits(torch, sink) == ([7, 23, 39, 55], [KEY_I32] * 4)
 
 
 @pytest.mark.parametrize("unroll", [4, 8, 16])
