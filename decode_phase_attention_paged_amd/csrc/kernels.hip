@@ -207,6 +207,16 @@ __device__ __forceinline__ void i8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
   hi = as_h2(c) - bias;
 }
 
+// The same four int8 values as 1152 + x, exactly, without the subtraction: the vector-ALU
+// consume takes 1152 times the sum of what it multiplies out once per load (scores) or
+// once per segment (outputs) instead of once per pair.
+constexpr float kI8Bias = 1152.0f;
+__device__ __forceinline__ void i8x4_to_h2_biased(uint32_t w, h2& lo, h2& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  lo = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));  // 1152 + x0, 1152 + x1
+  hi = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));  // 1152 + x2, 1152 + x3
+}
+
 // Four E4M3 codes (one dword, lowest address in the low byte) to two fp16 pairs. Every
 // finite E4M3 value is exact in fp16 (magnitudes 2^-9 .. 448), and the hardware conversion
 // (unit scale) maps the NaN codes to NaN.
@@ -216,7 +226,7 @@ __device__ __forceinline__ void fp8x4_to_h2(uint32_t w, h2& lo, h2& hi) {
 }
 
 // A load's elements as exact fp16 pairs (fp16, int8 and fp8 storage; bf16 values are not
-// all fp16 values and take their own path).
+// all fp16 values and take their own path). INT8 elements come out as 1152 + x.
 template <KvType kKv, int kGroup>
 __device__ __forceinline__ void unpack(const typename Geo<kKv, kGroup>::Load& raw,
                                        h2 (&x)[Geo<kKv, kGroup>::kPairs]) {
@@ -227,7 +237,7 @@ __device__ __forceinline__ void unpack(const typename Geo<kKv, kGroup>::Load& ra
     for (int e = 0; e < kWords; ++e) x[e] = as_h2(raw[e]);
   } else if constexpr (kKv == KvType::kI8) {
 #pragma unroll
-    for (int e = 0; e < kWords; ++e) i8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
+    for (int e = 0; e < kWords; ++e) i8x4_to_h2_biased(raw[e], x[2 * e], x[2 * e + 1]);
   } else {
 #pragma unroll
     for (int e = 0; e < kWords; ++e) fp8x4_to_h2(raw[e], x[2 * e], x[2 * e + 1]);
@@ -236,6 +246,7 @@ __device__ __forceinline__ void unpack(const typename Geo<kKv, kGroup>::Load& ra
 
 // q . k over this lane's elements of one load, accumulated in fp32 onto d. The query pairs
 // hold the query's raw 16-bit patterns: fp16 for every format but bf16, whose q is bf16.
+// For INT8 this is q . (k + 1152); the caller takes off 1152 times the sum of the q pairs.
 template <KvType kKv, int kGroup>
 __device__ __forceinline__ float dot_row(const typename Geo<kKv, kGroup>::Load& raw,
                                          const h2 (&q)[Geo<kKv, kGroup>::kPairs]) {
@@ -255,7 +266,8 @@ __device__ __forceinline__ float dot_row(const typename Geo<kKv, kGroup>::Load& 
   return d;
 }
 
-// acc[j] += w * v[j] over this lane's elements of one load.
+// acc[j] += w * v[j] over this lane's elements of one load (for INT8, w * (v[j] + 1152): the
+// state keeps the sum of the weights and takes 1152 times it off when the outputs leave).
 template <KvType kKv, int kGroup>
 __device__ __forceinline__ void axpy_row(const typename Geo<kKv, kGroup>::Load& raw, float w,
                                          float (&acc)[Geo<kKv, kGroup>::kChunk]) {
@@ -376,6 +388,7 @@ struct State {
   float m[kGroup];
   float l[kGroup];
   float acc[kGroup][Geo<kKv, kGroup>::kChunk];
+  float wsum[kGroup];   // INT8: sum of the weights folded into acc (rescaled and merged alike)
 };
 
 template <KvType kKv, int kGroup>
@@ -384,8 +397,23 @@ __device__ __forceinline__ void reset(State<kKv, kGroup>& st) {
   for (int h = 0; h < kGroup; ++h) {
     st.m[h] = kNegInf;
     st.l[h] = 0.0f;
+    st.wsum[h] = 0.0f;
 #pragma unroll
     for (int j = 0; j < Geo<kKv, kGroup>::kChunk; ++j) st.acc[h][j] = 0.0f;
+  }
+}
+
+// The outputs of an INT8 state without the 1152 offset of its values (once per segment).
+template <KvType kKv, int kGroup>
+__device__ __forceinline__ void unbias(State<kKv, kGroup>& st) {
+  if constexpr (kKv == KvType::kI8) {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+#pragma unroll
+      for (int j = 0; j < Geo<kKv, kGroup>::kChunk; ++j)
+        st.acc[h][j] = fmaf(-kI8Bias, st.wsum[h], st.acc[h][j]);
+      st.wsum[h] = 0.0f;
+    }
   }
 }
 
@@ -398,7 +426,8 @@ using QRegs = h2[kGroup][Geo<kKv, kGroup>::kPairs];
 // only read: masking works on copies.
 template <KvType kKv, int kGroup, bool kMasked>
 __device__ __forceinline__ void consume_tile(const Tile<kKv, kGroup>& t, State<kKv, kGroup>& st,
-                                             const QRegs<kKv, kGroup>& qh, float scale_log2,
+                                             const QRegs<kKv, kGroup>& qh,
+                                             const float (&qsum)[kGroup], float scale_log2,
                                              int row, int valid) {
   using Gm = Geo<kKv, kGroup>;
   bool ok[Gm::kLoads];
@@ -411,7 +440,8 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv, kGroup>& t, State<k
     if constexpr (Gm::kScaled) f *= t.ks[i];
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      const float d = dot_row<kKv, kGroup>(t.k[i], qh[h]);
+      float d = dot_row<kKv, kGroup>(t.k[i], qh[h]);
+      if constexpr (kKv == KvType::kI8) d = fmaf(-kI8Bias, qsum[h], d);
       const float sc = row_sum<Gm::kLanesPerRow>(d) * f;
       s[h][i] = ok[i] ? sc : kNegInf;
     }
@@ -434,6 +464,7 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv, kGroup>& t, State<k
     st.l[h] = st.l[h] * alpha + sum;
 #pragma unroll
     for (int j = 0; j < Gm::kChunk; ++j) st.acc[h][j] *= alpha;
+    if constexpr (kKv == KvType::kI8) st.wsum[h] *= alpha;
     st.m[h] = m_new;
   }
 #pragma unroll
@@ -447,16 +478,17 @@ __device__ __forceinline__ void consume_tile(const Tile<kKv, kGroup>& t, State<k
       float pw = p[h][i];
       if constexpr (Gm::kScaled) pw *= vscale;
       axpy_row<kKv, kGroup>(raw, pw, st.acc[h]);
+      if constexpr (kKv == KvType::kI8) st.wsum[h] += pw;
     }
   }
 }
 
 template <KvType kKv, int kGroup>
 __device__ __forceinline__ void consume(const Tile<kKv, kGroup>& t, State<kKv, kGroup>& st,
-                                        const QRegs<kKv, kGroup>& qh, float scale_log2, int row,
-                                        int valid) {
-  if (valid == kBlockSize) consume_tile<kKv, kGroup, false>(t, st, qh, scale_log2, row, kBlockSize);
-  else consume_tile<kKv, kGroup, true>(t, st, qh, scale_log2, row, valid);
+                                        const QRegs<kKv, kGroup>& qh, const float (&qsum)[kGroup],
+                                        float scale_log2, int row, int valid) {
+  if (valid == kBlockSize) consume_tile<kKv, kGroup, false>(t, st, qh, qsum, scale_log2, row, kBlockSize);
+  else consume_tile<kKv, kGroup, true>(t, st, qh, qsum, scale_log2, row, valid);
 }
 
 // Merge the (m, l, acc) of the lane `off` away into this lane's, for every head.
@@ -471,6 +503,7 @@ __device__ __forceinline__ void merge_lanes(State<kKv, kGroup>& st, int off) {
     const float wa = fast_exp2(st.m[h] - base);
     const float wb = fast_exp2(mo - base);
     st.l[h] = st.l[h] * wa + lo * wb;
+    if constexpr (kKv == KvType::kI8) st.wsum[h] = st.wsum[h] * wa + __shfl_xor(st.wsum[h], off) * wb;
 #pragma unroll
     for (int j = 0; j < Geo<kKv, kGroup>::kChunk; ++j) {
       const float ao = __shfl_xor(st.acc[h][j], off);
@@ -772,6 +805,7 @@ struct Path {
   using Gm = Geo<kKv, kGroup>;
   struct QV {
     QRegs<kKv, kGroup> v;
+    float sum[kGroup];   // INT8: this lane's sum of each head's q elements
   };
   using TileT = typename std::conditional<kMf, MTile<kKv>, Tile<kKv, kGroup>>::type;
   using StateT = typename std::conditional<kMf, MState, State<kKv, kGroup>>::type;
@@ -789,7 +823,7 @@ struct Path {
   __device__ __forceinline__ static void consume_unit(const TileT& t, StateT& st, const QT& q,
                                                       float scale_log2, int lane, int valid) {
     if constexpr (kMf) mconsume<kKv>(t, st, q, scale_log2, lane, valid);
-    else consume<kKv, kGroup>(t, st, q.v, scale_log2, lane / Gm::kLanesPerRow, valid);
+    else consume<kKv, kGroup>(t, st, q.v, q.sum, scale_log2, lane / Gm::kLanesPerRow, valid);
   }
   // Query operand of a segment whose G query rows (head-major, fp16 or bf16) are at `rows`.
   __device__ __forceinline__ static void load_q(QT& q, const u32x4* rows, int lane) {
@@ -805,6 +839,16 @@ struct Path {
 #pragma unroll
           for (int e = 0; e < 4; ++e) q.v[h][c * 4 + e] = as_h2(raw[e]);
         }
+      if constexpr (kKv == KvType::kI8) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int e = 0; e < Gm::kPairs; ++e)
+            sum += static_cast<float>(q.v[h][e].x) + static_cast<float>(q.v[h][e].y);
+          q.sum[h] = sum;
+        }
+      }
     }
   }
   // The wave's state for the merge across waves: per head its running max (log2 units),
@@ -815,6 +859,7 @@ struct Path {
       mpublish<kGroup>(st, acc, m, l, lane);
     } else {
       merge_rows<kKv, kGroup>(st);
+      unbias<kKv, kGroup>(st);
       const int row = lane / Gm::kLanesPerRow;
       const int col = lane % Gm::kLanesPerRow;
       if (row == 0) {
@@ -857,6 +902,7 @@ struct Path {
       }
     } else {
       merge_rows<kKv, kGroup>(st);
+      unbias<kKv, kGroup>(st);
       const int row = lane / Gm::kLanesPerRow;
       const int col = lane % Gm::kLanesPerRow;
 #pragma unroll
