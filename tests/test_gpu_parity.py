@@ -427,6 +427,30 @@ def test_fp8_small_integers_match_int8_bitwise(torch, lib):
     assert_parity(a, oracle_run(w)[0], "int8 integers")
 
 
+def test_fp8_and_int8_small_integers_agree_on_the_vector_consume(torch, lib):
+    # With one query head per KV head the vector consume runs: FP8 widens its codes to the
+    # exact integers, INT8 carries them as 1152 + x and takes the offset off per load and
+    # per segment. Both must agree to rounding (the offset's fp32 rounding is far below the
+    # parity tolerance), in every plan mode, and both must match the oracle.
+    table = oracle.e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    code_of = {int(v): c for c, v in enumerate(table)
+               if np.isfinite(v) and v == int(v) and abs(v) <= 16 and not (v == 0 and c)}
+    cfg = SMALL.with_(kv_dtype="int8", n_q_heads=4, n_kv_heads=4)
+    w = generate(cfg, seed=19)
+    rng = np.random.default_rng(19)
+    ints = [rng.integers(-16, 17, size=w.k_pages.shape) for _ in range(2)]
+    w.k_pages, w.v_pages = (i.astype(np.int8) for i in ints)
+    ref = oracle_run(w)[0]
+    for plan in (dict(), dict(num_workgroups=3), dict(num_splits=1), dict(num_splits=3)):
+        a, la = gpu_run(torch, lib, w, **plan)
+        w8 = generate(cfg, seed=19)
+        w8.k_pages, w8.v_pages = (np.vectorize(code_of.get)(i).astype(np.uint8) for i in ints)
+        b, lb = gpu_run(torch, lib, w8, **plan)
+        np.testing.assert_allclose(a, b, rtol=1e-4, atol=1e-4, err_msg=f"{plan}")
+        np.testing.assert_allclose(la, lb, rtol=1e-4, atol=1e-4, err_msg=f"{plan}")
+        assert_parity(a, ref, f"int8 integers, {plan}")
+
+
 def test_fp8_subnormal_codes_are_not_flushed(torch, lib):
     # One key per sequence made of subnormal codes (exponent field 0, values m/8 * 2^-6)
     # with a large row scale, so its score dominates only if the subnormals survive the
