@@ -901,6 +901,20 @@ def bench_prefill(args, cfg, lib, torch, np, binding, generate):
     print(json.dumps(record), flush=True)
 
 
+def decode_step_tiles(cfg, np):
+    """The (page, KV head) tiles one decode step of the workload reads, as tile indices
+    page * n_kv_heads + head in the order of the sequences and heads, and the number of
+    tiles in its pool."""
+    from decode_phase_attention_paged_amd.workload import layout
+    lens, table, num_pages = layout(cfg)
+    hkv = cfg.n_kv_heads
+    nb = -(-lens.astype(np.int64) // cfg.block_size)
+    parts = [table[b, :nb[b]].astype(np.int64) * hkv + g
+             for b in range(cfg.batch) for g in range(hkv)]
+    tiles = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    return tiles.astype(np.int32), num_pages * hkv
+
+
 def bench_hbm(args, cfg, torch, np, binding):
     """Reference read rates for the HBM roofline (decode_attn_hbm_reference): a random
     gather of the K and V tiles of one decode step of the workload (every (sequence, KV
@@ -910,19 +924,13 @@ def bench_hbm(args, cfg, torch, np, binding):
     pools rotate over replicas of at least 1 GiB in all, as in the decode bench, so the
     Infinity Cache cannot serve them. Prints one JSON line; `best_gather_gbs` is the
     attainable rate the decode kernels' roofline fraction can be read against."""
-    from decode_phase_attention_paged_amd.workload import layout
     elem = 2 if cfg.kv_dtype in ("fp16", "bf16") else 1
     tile_bytes = cfg.head_dim * cfg.block_size * elem
     if cfg.head_dim != 128 or cfg.block_size != 16:
         raise SystemExit("the reference gather reads the tiles of head_dim 128, 16-token pages")
     kind = binding.HBM_GATHER if elem == 2 else binding.HBM_GATHER_SCALED
-    lens, table, num_pages = layout(cfg)
-    hkv = cfg.n_kv_heads
-    nb = -(-lens.astype(np.int64) // cfg.block_size)
-    tiles = np.concatenate([table[b, :nb[b]].astype(np.int64) * hkv + g
-                            for b in range(cfg.batch) for g in range(hkv)]).astype(np.int32)
+    tiles, pool_tiles = decode_step_tiles(cfg, np)
     count = int(tiles.size)
-    pool_tiles = num_pages * hkv
     record = 64 if elem == 1 else 0
     pool_bytes = 2 * pool_tiles * (tile_bytes + record)
     reps = replicas_for(args, pool_bytes)

@@ -193,3 +193,24 @@ def test_summarize_hbm_reference_on_synthetic_output(tmp_path, monkeypatch):
     assert "best_stream_gbs: 7100.0" in text
     assert "-- python3 $REPO/bench.py --op hbm --steps 10" in text
     assert f"kernel_source_sha256: {bench.kernel_source_hash(bench.HBM_SOURCES)}" in text
+
+
+@pytest.mark.parametrize("index", [2, 3, 5, 10])
+def test_reference_gather_reads_each_tile_of_a_step_once(index):
+    """The reference gather's index list is exactly the set of (page, KV head) tiles one
+    decode step of the workload touches: every page of every sequence's table, for every
+    KV head, once."""
+    import numpy as np
+    from decode_phase_attention_paged_amd.workload import CONFIGS, layout
+    cfg = CONFIGS[index]
+    tiles, pool_tiles = bench.decode_step_tiles(cfg, np)
+    lens, table, num_pages = layout(cfg)
+    hkv = cfg.n_kv_heads
+    assert pool_tiles == num_pages * hkv
+    expect = {int(table[b, j]) * hkv + g for b in range(cfg.batch)
+              for j in range(-(-int(lens[b]) // cfg.block_size)) for g in range(hkv)}
+    assert tiles.dtype == np.int32 and len(tiles) == len(expect)
+    assert set(tiles.tolist()) == expect
+    assert tiles.min() >= 0 and tiles.max() < pool_tiles
+    # the workloads use every page of their pool
+    assert len(expect) == pool_tiles
