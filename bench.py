@@ -931,22 +931,22 @@ def bench_hbm(args, cfg, torch, np, binding):
     kind = binding.HBM_GATHER if elem == 2 else binding.HBM_GATHER_SCALED
     tiles, pool_tiles = decode_step_tiles(cfg, np)
     count = int(tiles.size)
-    record = 64 if elem == 1 else 0
-    pool_bytes = 2 * pool_tiles * (tile_bytes + record)
+    scale_bytes = 64 if elem == 1 else 0
+    pool_bytes = 2 * pool_tiles * (tile_bytes + scale_bytes)
     reps = replicas_for(args, pool_bytes)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     k = torch.zeros(reps * pool_tiles * tile_bytes, dtype=torch.uint8, device=dev)
     v = torch.zeros_like(k)
     ks = vs = None
-    if record:
-        ks = torch.zeros(reps * pool_tiles * record, dtype=torch.uint8, device=dev)
+    if scale_bytes:
+        ks = torch.zeros(reps * pool_tiles * scale_bytes, dtype=torch.uint8, device=dev)
         vs = torch.zeros_like(ks)
     tile_lists = [torch.from_numpy(tiles + r * pool_tiles).to(dev) for r in range(reps)]
     buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(65535 * 256, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    gather_bytes = 2 * count * (tile_bytes + record)
+    gather_bytes = 2 * count * (tile_bytes + scale_bytes)
     results = {"gather": [], "stream": []}
 
     def measure(kind, depth, nt, grid):
@@ -990,7 +990,7 @@ def bench_hbm(args, cfg, torch, np, binding):
         "repeats": args.repeats,
         "argv": sys.argv[1:],
         "config": {"workload": cfg.name, "kv_dtype": cfg.kv_dtype, "tile_bytes": tile_bytes,
-                   "scale_record_bytes": record, "tile_pairs_per_launch": count,
+                   "scale_record_bytes": scale_bytes, "tile_pairs_per_launch": count,
                    "gather_bytes_per_launch": gather_bytes, "pool_tiles": pool_tiles,
                    "replicas": reps, "stream_bytes_per_launch": buf.numel()},
         "gather": results["gather"],
