@@ -37,7 +37,10 @@
  * exact fp16 products (codes widened exactly; bf16 products for a BF16 cache) summed in
  * fp32, the weighted sum of V with each softmax weight rounded to fp16 (relative error at
  * most 2^-11), or for a BF16 cache split into two bf16 parts (at most 2^-16); the
- * normaliser adds the unrounded fp32 weights. With G <= 2 the weights stay fp32.
+ * normaliser adds the unrounded fp32 weights. With G <= 2 the weights stay fp32; there an
+ * INT8 code enters as the exact fp16 value 1152 + x, and 1152 times the sum of the query
+ * (per load) or of the weights (per segment) is taken off, which adds fp32 rounding of
+ * about 2^-24 * 1152 * sqrt(L_b) of a value's row scale.
  *
  * Memory layout (all row-major and contiguous; all tensor pointers are DEVICE pointers
  * owned by the caller, for example torch tensors; the library never frees them):
