@@ -17,13 +17,17 @@ clocks are up), then `repeats` windows of exactly --steps back-to-back steps,
 each between one pair of HIP events on the launch stream with a device synchronisation
 on both sides. `value` and `us_per_step` are the median window; the spread is reported.
 
-Prints one JSON line on stdout; progress goes to stderr.
+Prints one JSON line on stdout; progress goes to stderr. --op append, prefill and step
+time the other entry points on their workloads; --op hbm measures the reference reads
+(decode_attn_hbm_reference) on the workload's tiles: the attainable HBM rate that the
+roofline record's `attainable` field compares the step with.
 
     python bench.py --summarize-profile DIR --tag TAG
 
 turns the rocprofv3 CSVs of one profiled workload (kernel trace, FETCH_SIZE, WRITE_SIZE
 and the counter passes, in the directory layout the summary lists) into
-profiles/<op>_<workload>.txt.
+profiles/<op>_<workload>.txt (for --op hbm, the kernel trace alone into
+profiles/hbm_reference_<workload>.txt).
 """
 
 from __future__ import annotations
