@@ -451,6 +451,26 @@ def test_fp8_and_int8_small_integers_agree_on_the_vector_consume(torch, lib):
         assert_parity(a, ref, f"int8 integers, {plan}")
 
 
+@pytest.mark.parametrize("plan", [dict(), dict(num_splits=1), dict(num_workgroups=64)],
+                         ids=["auto", "segment", "stream"])
+def test_int8_offset_over_a_long_cache(torch, lib, plan):
+    # The INT8 vector consume adds w (v + 1152) and takes 1152 Σw off once per segment, so
+    # its fp32 rounding grows with the cache: at most about 2^-24 · 1152 · √L of a row
+    # scale per output, 3.5e-4 here (65 536 tokens, scales at their largest, 0.02), against
+    # the 2e-3 absolute bound (measured: below 1e-5 in every mode). One sequence per KV head
+    # runs as one segment, as partitions or as stream runs.
+    cfg = Config(0, "long_int8_mha", batch=1, n_q_heads=4, n_kv_heads=4, head_dim=128,
+                 block_size=16, len_lo=65536, len_hi=65536, kv_dtype="int8")
+    w = generate(cfg, seed=23)
+    w.k_scale = np.full_like(w.k_scale, 0.02)
+    w.v_scale = np.full_like(w.v_scale, 0.02)
+    got, lse = gpu_run(torch, lib, w, **plan)
+    ref, ref_lse = oracle_run(w)
+    assert_parity(got, ref, f"int8, 65536 tokens, {plan}")
+    assert np.abs(got.astype(np.float64) - ref).max() < 1e-3
+    assert_lse(lse, ref_lse, f"int8, 65536 tokens, {plan}")
+
+
 def test_fp8_subnormal_codes_are_not_flushed(torch, lib):
     # One key per sequence made of subnormal codes (exponent field 0, values m/8 * 2^-6)
     # with a large row scale, so its score dominates only if the subnormals survive the
