@@ -149,6 +149,36 @@ def test_edge_lengths_and_nan_canaries(torch, lib, kv):
         assert np.all(got[lens == 0] == 0)
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_seeded_random_shapes(torch, lib, case):
+    # Seeded draws over formats, group sizes, KV head counts, batch sizes, length mixes
+    # (empty caches included), softmax scales, unreferenced pages and plans, every slot no
+    # token owns holding NaN.
+    rng = np.random.default_rng(700 + case)
+    kv = KVS[case % 4]
+    group = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.integers(1, 5))
+    batch = int(rng.integers(1, 41))
+    hi = int(rng.integers(1, 1200))
+    cfg = SMALL.with_(kv_dtype=kv, batch=batch, n_q_heads=group * hkv, n_kv_heads=hkv,
+                      len_lo=0, len_hi=hi, scale=float(rng.uniform(0.02, 0.3)))
+    # Lengths: uniform, with about one in six empty and one in six a whole number of pages.
+    lens = rng.integers(0, hi + 1, size=batch)
+    pick = rng.random(batch)
+    lens = np.where(pick < 1 / 6, 0, np.where(pick < 2 / 6, 16 * (lens // 16), lens))
+    w = generate(cfg, seed=800 + case, poison=True, extra_pages=int(rng.integers(0, 4)),
+                 seq_lens=lens.astype(np.int32))
+    plan = PLANS[int(rng.integers(0, len(PLANS)))]
+    print(f"case decode random {case}: {kv} G={group} Hkv={hkv} B={batch} "
+          f"lens={w.seq_lens.tolist()} plan={plan}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    got, lse = gpu_run(torch, lib, w, **plan)
+    assert np.isfinite(got).all(), f"{plan}: a NaN canary leaked into the output"
+    assert_parity(got, ref, f"random case {case}")
+    assert_lse(lse, ref_lse, f"random case {case}")
+    assert np.all(got[w.seq_lens == 0] == 0)
+
+
 @pytest.mark.parametrize("kv,group", [("fp16", 1), ("fp16", 2), ("int8", 4), ("fp8", 8)])
 def test_segment_mode_full_and_partial_rounds(torch, lib, kv, group):
     # 160 segments dealt in a snake over grids that leave the last round full, partial or a
