@@ -190,3 +190,40 @@ def test_three_steps_then_attention(torch, lib, kv):
     want, _ = oracle.decode_attention(w.q, ref[0], ref[1], table, grown, w.scale, ref[2], ref[3])
     diff = np.abs(host(out).astype(np.float64) - want)
     assert np.all(diff <= ATOL + RTOL * np.abs(want)), f"max|d|={diff.max():.3e}"
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_random_appends(torch, lib, case):
+    # Seeded draws over formats, KV head counts, batch sizes, lengths and positions (some
+    # sequences without a new token), with awkward rows among the new ones: all elements
+    # equal, all tiny, one large element among small ones, alternating signs. The written
+    # pools must stay bit-identical to the oracle's.
+    kv = ["fp16", "int8", "bf16", "fp8"][case % 4]
+    rng = np.random.default_rng(900 + case)
+    hkv = int(rng.integers(1, 9))
+    cfg = CONFIGS[1].with_(batch=int(rng.integers(1, 61)), n_q_heads=hkv, n_kv_heads=hkv,
+                           len_lo=0, len_hi=int(rng.integers(1, 400)), kv_dtype=kv)
+    w, table, lens, pools, scales, new = grown_cache(cfg, 950 + case, rng)
+    positions = lens.copy().astype(np.int32)
+    positions[rng.random(cfg.batch) < 0.2] = -1
+    positions[positions >= cfg.max_blocks_per_seq * cfg.block_size] = -1   # no page for it
+    d = cfg.head_dim
+    awkward = [np.full(d, 0.75, np.float32), np.full(d, 3e-5, np.float32),
+               np.where(np.arange(d) == 7, 900.0, 0.01).astype(np.float32),
+               np.where(np.arange(d) % 2 == 0, 1.5, -1.5).astype(np.float32)]
+    for i, row in enumerate(awkward):
+        b, g = int(rng.integers(0, cfg.batch)), int(rng.integers(0, hkv))
+        enc = (row.view(np.uint32) >> 16).astype(np.uint16) if kv == "bf16" else row.astype(np.float16)
+        new[i % 2][b, g] = enc
+    print(f"case append random {case}: {kv} Hkv={hkv} B={cfg.batch} "
+          f"positions={positions.tolist()}", flush=True)
+    got = run_append(torch, lib, table, positions, pools, scales, new)
+    want = oracle.append_kv(pools[0], pools[1], table, positions, new[0], new[1],
+                            cfg.block_size, scales[0], scales[1])
+    for g, x, what in zip(got, want, ("k_pages", "v_pages", "k_scale", "v_scale")):
+        if x is None:
+            assert g is None
+            continue
+        bits = {1: np.uint8, 2: np.uint16, 4: np.uint32}[g.itemsize]
+        bad = np.argwhere(g.view(bits) != x.view(bits))
+        assert bad.size == 0, f"{what}: {len(bad)} elements differ, first at {bad[:3].tolist()}"
