@@ -300,6 +300,34 @@ def test_segment_mode_restages_query_rows(torch, lib, kv, group):
         assert_lse(lse, ref_lse, "lse")
 
 
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+@pytest.mark.parametrize("group", [1, 4])
+def test_batches_beyond_4096_sequences(torch, lib, kv, group):
+    # 4500 sequences of 0-100 tokens (ties and empty caches common; the unused slots of
+    # each last page and the spare pages hold NaN). Past 4096 sequences segment mode takes
+    # the segments in index order with lengths through scalar loads; it runs on the library's
+    # grid and on 3 workgroups (3000 segments each), and split mode on two partitions.
+    # Stream mode keeps the batch's page counts in LDS and refuses such a batch.
+    batch = 4500
+    choices = np.array([0, 1, 16, 17, 40, 64, 100], dtype=np.int32)
+    lens = np.random.default_rng(batch + group).choice(choices, size=batch)
+    cfg = SMALL.with_(kv_dtype=kv, batch=batch, n_q_heads=2 * group, n_kv_heads=2, len_lo=0,
+                      len_hi=int(choices.max()))
+    w = generate(cfg, seed=70 + group, seq_lens=lens, poison=True, extra_pages=2)
+    print(f"case batch {batch} kv={kv} G={group}", flush=True)
+    ref, ref_lse = oracle_run(w)
+    d = to_dev(torch, w)
+    for name, plan in (("auto", {}), ("segment grid 3", dict(num_splits=1, num_workgroups=3)),
+                       ("split 2", dict(num_splits=2))):
+        got, lse = gpu_run(torch, lib, w, dev_inputs=d, **plan)
+        assert np.isfinite(got).all(), f"{name}: a NaN canary leaked into the output"
+        assert_parity(got, ref, f"batch {batch} {kv} G={group} {name}")
+        assert_lse(lse, ref_lse, name)
+    with pytest.raises(lib.DecodeAttnError) as err:
+        gpu_run(torch, lib, w, dev_inputs=d, num_workgroups=64)
+    assert err.value.status == 2    # DECODE_ATTN_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("plan", [dict(num_workgroups=2), dict(num_splits=2),
                                   dict(num_splits=1, num_workgroups=2)],
                          ids=["wg2", "split2", "seg2"])
